@@ -1,0 +1,203 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE FFN layer forward on one MI355X.
+
+A step is one whole-layer forward (RMSNorm + gate, top-k, sort, grouped
+expert GEMMs, reduce, shared expert, residual) over one batch of seeded
+synthetic tokens already resident in HBM. Eight layer instances with
+distinct weights run round-robin, as consecutive layers of a model would,
+so the weight stream cannot sit in the 256 MB Infinity Cache. Each step has
+its own input buffer (the forward is in place), prepared before timing.
+
+Prints ONE JSON line. The roofline object covers the dominant kernel (the
+slower of the grouped up / grouped down GEMMs), timed with HIP events on the
+stream it runs on over the timed region. The cpu_baseline object times the
+float64 oracle on a bounded token sample of the same workload on the host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+METRIC = ("MoE-layer prefill tokens/s at N=1024 bf16; % MFMA peak (GEMM) / "
+          "% HBM peak (N≤16)")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="nemotron_direct_bf16")
+    ap.add_argument("--tokens", type=int, default=None, help="override N of the workload")
+    ap.add_argument("--instances", type=int, default=8)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--all-stages", action="store_true",
+                    help="record every stage (adds event markers to the timed region)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "the layer's tokens shard with no exchange, and multi-GPU runs are not part "
+              "of this build", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from mixture_experts_ffn_gate_amd import workloads as wlm
+    from mixture_experts_ffn_gate_amd import moe_layer as ml
+
+    wl = wlm.WORKLOADS[args.workload]
+    if args.tokens:
+        wl = wl.with_(N=args.tokens)
+    N = wl.N
+    torch.cuda.init()
+    dev = torch.device("cuda:0")
+    log(f"[bench] workload {wl.name} N={N} instances={args.instances} "
+        f"steps={args.steps} warmup={args.warmup}")
+
+    # Layers (weights generated on the device, copied into each layer, freed).
+    layers = []
+    host_w0 = None
+    for i in range(args.instances):
+        W = wlm.make_weights(wl, seed=args.seed + i, device=dev)
+        layers.append(ml.layer_from_workload(wl, W, max_tokens=N))
+        if i == 0 and not args.no_cpu_baseline:
+            host_w0 = {k: wlm.to_numpy_f32(v) for k, v in W.items()}
+        del W
+    torch.cuda.synchronize()
+    log("[bench] layers built")
+
+    # One pristine input per step.
+    base = [wlm.make_hidden(wl, N, seed=args.seed + i, device=dev)[0]
+            for i in range(args.instances)]
+    total = args.warmup + args.steps
+    inputs = [base[j % args.instances].clone() for j in range(total)]
+    residual = torch.empty_like(inputs[0])
+    x0_host = wlm.to_numpy_f32(base[0]) if host_w0 is not None else None
+    torch.cuda.synchronize()
+
+    for j in range(args.warmup):
+        layers[j % args.instances].forward(inputs[j], residual)
+    torch.cuda.synchronize()
+
+    stages = ml.STAGES if args.all_stages else ("grouped_up", "grouped_down")
+    for L in layers:
+        L.timing_begin(stages, max_forwards=args.steps)
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    ev0.record(stream)
+    for j in range(args.warmup, total):
+        layers[j % args.instances].forward(inputs[j], residual)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+
+    # Per-stage event times, summed over all instances.
+    st_tot = {}
+    for L in layers:
+        for st, (ms, cnt) in L.timing_end().items():
+            a = st_tot.setdefault(st, [0.0, 0])
+            a[0] += ms
+            a[1] += cnt
+    stage_us = {st: 1000.0 * v[0] / v[1] for st, v in st_tot.items() if v[1]}
+    log("[bench] stage averages (us): " + ", ".join(f"{k}={v:.1f}" for k, v in stage_us.items()))
+
+    # Routing statistics of each instance (touched experts drive the weight bytes).
+    touched = []
+    max_load = []
+    for L in layers:
+        c = torch.empty(wl.E, dtype=torch.int32, device=dev)
+        L.debug_read("counts", c)
+        c = c.cpu().numpy()
+        touched.append(int((c > 0).sum()))
+        max_load.append(int(c.max()))
+    E_t = float(np.mean(touched))
+    R = N * wl.k
+    D, I = wl.D, wl.I
+    wbytes = E_t * I * D * 2
+    algo = {
+        "grouped_up": wbytes + N * D * 2 + R * I * 2,
+        "grouped_down": wbytes + R * I * 2 + R * D * 4,
+    }
+    flops = {"grouped_up": 2.0 * R * D * I, "grouped_down": 2.0 * R * D * I}
+    dom = max(("grouped_up", "grouped_down"), key=lambda s: stage_us.get(s, 0.0))
+    dom_s = stage_us[dom] * 1e-6
+    achieved = algo[dom] / dom_s / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": dom, "avg_us": round(stage_us[dom], 2),
+                "algorithmic_bytes": int(algo[dom]),
+                "mfma_tflops": round(flops[dom] / dom_s / 1e12, 1),
+                "mfma_frac": round(flops[dom] / dom_s / 1e12 / BF16_PEAK_TFLOPS, 4)}
+
+    tokens_per_s = N * args.steps / (ms_total / 1000.0)
+    layer_flops = wl.flops(N)
+    layer_bytes = (E_t * I * D * 2 * 2 + wl.S * wl.H * 2 * 2 + wl.E * wl.H * 2
+                   + (wl.L * wl.H * 2 * 2 if wl.L else 0) + N * wl.H * 2 * 3)
+    out = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if wl.act_dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1/fan_in) weights, N(0,1) tokens)",
+        "config": {"workload": wl.name, "hidden": wl.H, "experts": wl.E, "top_k": wl.k,
+                   "moe_inter": wl.I, "shared_inter": wl.S, "latent": wl.L, "tokens": N,
+                   "expert_dtype": wl.expert_dtype, "layer_instances": args.instances,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "layer": {"tflops": round(layer_flops / (ms_step * 1e-3) / 1e12, 1),
+                  "gbs": round(layer_bytes / (ms_step * 1e-3) / 1e9, 1),
+                  "hbm_frac": round(layer_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "mfma_frac": round(layer_flops / (ms_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                                     4),
+                  "experts_touched": E_t, "max_expert_load": int(max(max_load)),
+                  "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
+                  "wall_s": round(t_wall, 3)},
+        "cpu_baseline": None,
+    }
+
+    if host_w0 is not None:
+        out["cpu_baseline"] = cpu_baseline(wl, host_w0, x0_host, args.cpu_sample_tokens)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline(wl, Wn, x, sample):
+    """The float64 oracle on the first ``sample`` tokens of instance 0, on the host."""
+    import threadpoolctl
+
+    from oracle import moe_oracle as mo
+
+    xs = x[:sample].astype("float64")
+    info = threadpoolctl.threadpool_info()
+    threads = max([d.get("num_threads", 1) for d in info] or [1])
+    t = time.perf_counter()
+    mo.layer_forward(xs, Wn, wl.oracle_cfg())
+    dt = time.perf_counter() - t
+    log(f"[bench] oracle: {xs.shape[0]} tokens in {dt:.2f} s with {threads} BLAS threads")
+    return {"value": round(xs.shape[0] / dt, 2), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"first {xs.shape[0]} tokens of layer instance 0 ({wl.name}), one "
+                      f"float64 oracle forward, {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,340 @@
+// GEMM kernels of the MoE layer on gfx950.
+//
+// Every projection of the layer is C[p][n] = sum_k A[arow(p)][k] * W[g][n][k]
+// followed by an epilogue: the grouped expert GEMMs (page "Struct MoeLayer",
+// `forward_prefill`: grouped up GEMM, activation, grouped down GEMM; each
+// expert's weights read once per prefill instead of once per token), the
+// shared expert and the fc1/fc2 latent projections (page
+// "metrale_model_arch/nemotron_moe.rs", `prefill`: dense GEMMs over all
+// tokens). relu^2 is fused into the up-projection epilogue (same page, module
+// doc: routed up, relu^2, down).
+//
+// bf16 MFMA kernel (gemm_mfma_kernel):
+//   * MFMA v_mfma_f32_16x16x32_bf16 with the WEIGHTS as the A operand (16
+//     output features) and the ACTIVATIONS as the B operand (16 tokens), so a
+//     lane's four results are four consecutive output features of one row:
+//     one 8-byte (bf16) or 16-byte (fp32) store.
+//   * Weights are re-tiled once at layer creation into the MFMA lane order:
+//     [N/16][K/32][64 lanes][8], lane l holding feature l%16 and k-elements
+//     8*(l/16)..+7 of its 16x32 block. A wave's weight fetch for one MFMA is
+//     then one contiguous 1 KiB read, and each weight byte is fetched by
+//     exactly one wave (waves own disjoint features).
+//   * A workgroup (4 waves) covers 4*WF features x BMT rows. The BMT x 64
+//     activation slice of each k-step is gathered (rows by the route
+//     permutation) with 16-byte loads, staged through LDS (double buffered,
+//     XOR-swizzled 16-byte chunks so the MFMA operand reads are conflict-free)
+//     and shared by the 4 waves.
+//   * Weights for step k+1 are in flight while step k computes.
+#include "kernels.h"
+
+// ---------------------------------------------------------------------------
+// Tile decode shared by both kernels.
+// ---------------------------------------------------------------------------
+struct TileInfo {
+  int g, row0, rows;
+};
+
+__device__ __forceinline__ bool decode_tile(const GemmArgs& a, int tile, int bmt, TileInfo& ti) {
+  if (a.tiles) {
+    if (tile >= *a.num_tiles) return false;
+    const int2 t = a.tiles[tile];
+    ti.g = t.x;
+    const int lo = a.offsets[t.x], hi = a.offsets[t.x + 1];
+    ti.row0 = lo + t.y;
+    ti.rows = min(bmt, hi - ti.row0);
+  } else {
+    ti.g = 0;
+    ti.row0 = tile * bmt;
+    ti.rows = min(bmt, a.M - ti.row0);
+  }
+  return ti.rows > 0;
+}
+
+__device__ __forceinline__ int a_row_of(const GemmArgs& a, int p) {
+  return a.a_rows ? a.a_rows[p] / a.a_div : p;
+}
+
+// ---------------------------------------------------------------------------
+// fp32 SIMT GEMM: 64x64 output tile, 256 threads with 4x4 outputs each, BK=16.
+// Used by fp32 layers (no fp32 MFMA shape is faster than this at their sizes).
+// ---------------------------------------------------------------------------
+template <int EPI>
+__global__ void __launch_bounds__(256) gemm_simt_f32_kernel(GemmArgs a) {
+  __shared__ float As[16][65];
+  __shared__ float Bs[16][65];
+  TileInfo ti;
+  if (!decode_tile(a, blockIdx.y, 64, ti)) return;
+  const int n0 = blockIdx.x * 64;
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const float* A = (const float*)a.A;
+  const float* B = (const float*)a.B + (size_t)ti.g * a.b_gstride;
+
+  // Loader: row (tid>>2) of the tile, k-quad (tid&3).
+  const int lr = tid >> 2, lk = (tid & 3) * 4;
+  const int arow = a_row_of(a, ti.row0 + min(lr, ti.rows - 1));
+  const float* asrc = A + (size_t)arow * a.lda + lk;
+  const int bn = min(n0 + lr, a.N - 1);
+  const float* bsrc = B + (size_t)bn * a.K + lk;
+
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < a.K; k0 += 16) {
+    float4 av = *(const float4*)(asrc + k0);
+    float4 bv = *(const float4*)(bsrc + k0);
+    As[lk + 0][lr] = av.x; As[lk + 1][lr] = av.y; As[lk + 2][lr] = av.z; As[lk + 3][lr] = av.w;
+    Bs[lk + 0][lr] = bv.x; Bs[lk + 1][lr] = bv.y; Bs[lk + 2][lr] = bv.z; Bs[lk + 3][lr] = bv.w;
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float ar[4], br[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { ar[i] = As[kk][ty * 4 + i]; br[i] = Bs[kk][tx * 4 + i]; }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] += ar[i] * br[j];
+    }
+    __syncthreads();
+  }
+  float* C = (float*)a.C;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = ty * 4 + i;
+    if (r >= ti.rows) continue;
+    const int p = ti.row0 + r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tx * 4 + j;
+      if (n >= a.N) continue;
+      float v = acc[i][j];
+      if (EPI == EPI_RELU2) v = relu2(v);
+      if (EPI == EPI_ADD_RES) {
+        v += ((const float*)a.res)[(size_t)p * a.ldc + n];
+        if (a.add) v += a.add[(size_t)p * a.ldc + n];
+      }
+      C[(size_t)p * a.ldc + n] = v;
+    }
+  }
+}
+
+hipError_t launch_gemm_simt_f32(const GemmArgs& a, int epi, int grid_y, hipStream_t s) {
+  dim3 grid((a.N + 63) / 64, grid_y);
+  switch (epi) {
+    case EPI_RELU2: hipLaunchKernelGGL(gemm_simt_f32_kernel<EPI_RELU2>, grid, dim3(256), 0, s, a); break;
+    case EPI_STORE: hipLaunchKernelGGL(gemm_simt_f32_kernel<EPI_STORE>, grid, dim3(256), 0, s, a); break;
+    case EPI_ADD_RES: hipLaunchKernelGGL(gemm_simt_f32_kernel<EPI_ADD_RES>, grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA GEMM.
+// ---------------------------------------------------------------------------
+template <typename TC> struct store4;
+template <> struct store4<float> {
+  static __device__ __forceinline__ void st(float* p, floatx4 v) { *(floatx4*)p = v; }
+  static __device__ __forceinline__ floatx4 ld(const float* p) { return *(const floatx4*)p; }
+};
+template <> struct store4<bf16> {
+  static __device__ __forceinline__ void st(bf16* p, floatx4 v) {
+    bf16x4 o;
+    o[0] = (bf16)v[0]; o[1] = (bf16)v[1]; o[2] = (bf16)v[2]; o[3] = (bf16)v[3];
+    *(bf16x4*)p = o;
+  }
+  static __device__ __forceinline__ floatx4 ld(const bf16* p) {
+    bf16x4 i = *(const bf16x4*)p;
+    floatx4 v;
+    v[0] = (float)i[0]; v[1] = (float)i[1]; v[2] = (float)i[2]; v[3] = (float)i[3];
+    return v;
+  }
+};
+
+template <int WF, int BMT, int EPI, typename TC>
+__global__ void __launch_bounds__(256) gemm_mfma_kernel(GemmArgs a) {
+  constexpr int FT = WF / 16;      // 16-feature tiles per wave
+  constexpr int TT = BMT / 16;     // 16-row tiles per workgroup
+  constexpr int BK = 64;           // k per step (two MFMA k-chunks of 32)
+  constexpr int CHUNKS = BMT * 8;  // 16-byte chunks of one activation slice
+  constexpr int LPASS = (CHUNKS + 255) / 256;
+  __shared__ __attribute__((aligned(16))) bf16 xs[2][BMT * BK];
+
+  TileInfo ti;
+  if (!decode_tile(a, blockIdx.y, BMT, ti)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nsteps = a.K / BK;
+  const int KC = a.K / 32;
+
+  // Activation loader: chunk c = tid + 256*i -> row c/8, 16-byte chunk c%8.
+  const bf16* asrc[LPASS];
+  int lds_off[LPASS];
+  bool lact[LPASS];
+#pragma unroll
+  for (int i = 0; i < LPASS; ++i) {
+    const int c = tid + 256 * i;
+    lact[i] = c < CHUNKS;
+    const int row = c >> 3, ch = c & 7;
+    const int r = min(row, ti.rows - 1);
+    const int arow = a_row_of(a, ti.row0 + r);
+    asrc[i] = (const bf16*)a.A + (size_t)arow * a.lda + ch * 8;
+    lds_off[i] = row * BK + ((ch ^ (row & 7)) << 3);
+  }
+
+  // Weight fragments of this wave: feature tile ft starts at nf0 + 16*ft.
+  const int nf0 = blockIdx.x * (4 * WF) + wave * WF;
+  const bf16* W = (const bf16*)a.B + (size_t)ti.g * a.b_gstride;
+  const bf16* wptr[FT];
+#pragma unroll
+  for (int ft = 0; ft < FT; ++ft) {
+    int rt = (nf0 >> 4) + ft;
+    if (rt * 16 >= a.N) rt = 0;  // dead tile: read valid memory, never stored
+    wptr[ft] = W + ((size_t)rt * KC * 64 + lane) * 8;
+  }
+
+  floatx4 acc[FT][TT];
+#pragma unroll
+  for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) acc[ft][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  bf16x8 wcur[FT][2], wnxt[FT][2];
+  bf16x8 areg[LPASS];
+
+  // Prologue: step 0 activations -> LDS buffer 0, step 0 weights -> registers.
+#pragma unroll
+  for (int i = 0; i < LPASS; ++i)
+    if (lact[i]) areg[i] = *(const bf16x8*)(asrc[i]);
+#pragma unroll
+  for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) wcur[ft][s] = *(const bf16x8*)(wptr[ft] + s * 512);
+#pragma unroll
+  for (int i = 0; i < LPASS; ++i)
+    if (lact[i]) *(bf16x8*)(&xs[0][lds_off[i]]) = areg[i];
+  __syncthreads();
+
+  const int brow = lane & 15, bch = lane >> 4;
+  for (int ks = 0; ks < nsteps; ++ks) {
+    const int cur = ks & 1;
+    const bool more = ks + 1 < nsteps;
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < LPASS; ++i)
+        if (lact[i]) areg[i] = *(const bf16x8*)(asrc[i] + (ks + 1) * BK);
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          wnxt[ft][s] = *(const bf16x8*)(wptr[ft] + ((size_t)(ks + 1) * 2 + s) * 512);
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      bf16x8 xf[TT];
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        const int row = tt * 16 + brow;
+        const int ch = s * 4 + bch;
+        xf[tt] = *(const bf16x8*)(&xs[cur][row * BK + ((ch ^ (row & 7)) << 3)]);
+      }
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+          acc[ft][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wcur[ft][s], xf[tt], acc[ft][tt],
+                                                                0, 0, 0);
+    }
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < LPASS; ++i)
+        if (lact[i]) *(bf16x8*)(&xs[cur ^ 1][lds_off[i]]) = areg[i];
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) wcur[ft][s] = wnxt[ft][s];
+    }
+    __syncthreads();
+  }
+
+  // Epilogue: lane holds features nf0 + 16*ft + 4*(lane/16) + 0..3 of row 16*tt + lane%16.
+  TC* C = (TC*)a.C;
+#pragma unroll
+  for (int ft = 0; ft < FT; ++ft) {
+    const int n = nf0 + ft * 16 + 4 * (lane >> 4);
+    if (n >= a.N) continue;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const int r = tt * 16 + (lane & 15);
+      if (r >= ti.rows) continue;
+      const int p = ti.row0 + r;
+      floatx4 v = acc[ft][tt];
+      if (EPI == EPI_RELU2) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = relu2(v[q]);
+      }
+      if (EPI == EPI_ADD_RES) {
+        v += store4<TC>::ld((const TC*)a.res + (size_t)p * a.ldc + n);
+        if (a.add) v += *(const floatx4*)(a.add + (size_t)p * a.ldc + n);
+      }
+      store4<TC>::st(C + (size_t)p * a.ldc + n, v);
+    }
+  }
+}
+
+template <int WF, int BMT>
+static hipError_t launch_mfma_shape(const GemmArgs& a, int epi, bool tc_bf16, int grid_y,
+                                    hipStream_t s) {
+  dim3 grid((a.N + 4 * WF - 1) / (4 * WF), grid_y);
+  if (tc_bf16) {
+    switch (epi) {
+      case EPI_RELU2: hipLaunchKernelGGL((gemm_mfma_kernel<WF, BMT, EPI_RELU2, bf16>), grid, dim3(256), 0, s, a); break;
+      case EPI_STORE: hipLaunchKernelGGL((gemm_mfma_kernel<WF, BMT, EPI_STORE, bf16>), grid, dim3(256), 0, s, a); break;
+      case EPI_ADD_RES: hipLaunchKernelGGL((gemm_mfma_kernel<WF, BMT, EPI_ADD_RES, bf16>), grid, dim3(256), 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (epi) {
+      case EPI_RELU2: hipLaunchKernelGGL((gemm_mfma_kernel<WF, BMT, EPI_RELU2, float>), grid, dim3(256), 0, s, a); break;
+      case EPI_STORE: hipLaunchKernelGGL((gemm_mfma_kernel<WF, BMT, EPI_STORE, float>), grid, dim3(256), 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_mfma(const GemmArgs& a, MfmaCfg cfg, int epi, bool tc_bf16, bool nvfp4,
+                            int grid_y, hipStream_t s) {
+  if (nvfp4) return hipErrorInvalidValue;  // NVFP4 weights use their own kernel
+  if (cfg.wf == 16 && cfg.bmt == 16) return launch_mfma_shape<16, 16>(a, epi, tc_bf16, grid_y, s);
+  if (cfg.wf == 32 && cfg.bmt == 32) return launch_mfma_shape<32, 32>(a, epi, tc_bf16, grid_y, s);
+  if (cfg.wf == 32 && cfg.bmt == 64) return launch_mfma_shape<32, 64>(a, epi, tc_bf16, grid_y, s);
+  if (cfg.wf == 32 && cfg.bmt == 128) return launch_mfma_shape<32, 128>(a, epi, tc_bf16, grid_y, s);
+  return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Re-tile [G][N][K] row-major bf16 into [G][N/16][K/32][64][8] (MFMA A-operand
+// lane order). One thread per 16-byte destination chunk.
+// ---------------------------------------------------------------------------
+__global__ void retile_bf16_kernel(const bf16* __restrict__ src, bf16* __restrict__ dst, int G,
+                                   int N, int K) {
+  const size_t chunks = (size_t)G * N * K / 8;
+  const int KC = K / 32, NT = N / 16;
+  for (size_t c = blockIdx.x * (size_t)blockDim.x + threadIdx.x; c < chunks;
+       c += (size_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(c & 63);
+    size_t blk = c >> 6;  // (g, rt, kc)
+    const int kc = (int)(blk % KC);
+    blk /= KC;
+    const int rt = (int)(blk % NT);
+    const size_t g = blk / NT;
+    const int row = rt * 16 + (lane & 15);
+    const int k = kc * 32 + 8 * (lane >> 4);
+    *(bf16x8*)(dst + c * 8) = *(const bf16x8*)(src + (g * N + row) * (size_t)K + k);
+  }
+}
+
+hipError_t launch_retile_bf16(const bf16* src, bf16* dst, int G, int N, int K, hipStream_t s) {
+  const size_t chunks = (size_t)G * N * K / 8;
+  const int blocks = (int)std::min<size_t>((chunks + 255) / 256, 65536);
+  hipLaunchKernelGGL(retile_bf16_kernel, dim3(blocks), dim3(256), 0, s, src, dst, G, N, K);
+  return hipGetLastError();
+}

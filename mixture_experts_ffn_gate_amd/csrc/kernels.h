@@ -1,0 +1,74 @@
+// Internal kernel launch interface of the MoE layer library (not part of the C ABI).
+#pragma once
+
+#include "common.h"
+#include "../../include/moe_layer.h"
+
+#define MOE_MAX_E 512
+
+// Epilogues of the GEMM kernels.
+enum {
+  EPI_RELU2 = 0,    // C = relu(acc)^2
+  EPI_STORE = 1,    // C = acc
+  EPI_ADD_RES = 2   // C = acc + res + add   (res in C's dtype, add fp32 or null)
+};
+
+// One GEMM launch: C[p][n] = sum_k A[arow(p)][k] * B[g][n][k], then the epilogue.
+//   dense   (tiles == null): rows p in [0, M), group g = 0
+//   grouped (tiles != null): tile i covers rows offsets[g] + r0 ...
+//            min(offsets[g] + r0 + bm, offsets[g+1]) where (g, r0) = tiles[i];
+//            only i < *num_tiles are live
+//   arow(p) = a_rows ? a_rows[p] / a_div : p   (gather of permuted activations)
+struct GemmArgs {
+  const void* A;
+  int lda;
+  const int* a_rows;
+  int a_div;
+  const void* B;            // bf16/f32: [G][N][K] (MFMA path: pre-tiled, see gemm.hip)
+  long long b_gstride;      // elements (bytes for NVFP4) between groups
+  const uint8_t* b_scales;  // NVFP4 block scales (pre-tiled)
+  long long bs_gstride;     // bytes between groups
+  const float* b_scale2;    // NVFP4 per-group scale2
+  void* C;
+  int ldc;
+  int M, N, K;
+  const int2* tiles;
+  const int* num_tiles;
+  const int* offsets;
+  int bm;
+  const void* res;
+  const float* add;
+};
+
+hipError_t launch_norm_gate(int act_dt, const void* hidden, const void* gamma, const void* wgate,
+                            void* normed, void* residual, float* logits, int n, int H, int E,
+                            float eps, hipStream_t s);
+hipError_t launch_topk(const float* logits, int n, int E, int k, float scale, int* ids, float* w,
+                       hipStream_t s);
+hipError_t launch_route_sort(const int* ids, int R, int E, int* counts, int* offsets, int* perm,
+                             int* inv, int bm, int2* tiles, int* num_tiles, hipStream_t s);
+
+// fp32 SIMT GEMM (64x64 tiles, bm must be 64 in grouped mode); C fp32.
+hipError_t launch_gemm_simt_f32(const GemmArgs& a, int epi, int grid_y, hipStream_t s);
+
+// bf16 MFMA GEMM. cfg selects the tile shape (see gemm.hip); C dtype by epilogue:
+// tc_bf16 = true stores bf16, else fp32.
+struct MfmaCfg {
+  int wf;   // features per wave (16, 32, 64)
+  int bmt;  // rows (tokens / routes) per workgroup tile (16, 32, 64, 128)
+};
+hipError_t launch_gemm_mfma(const GemmArgs& a, MfmaCfg cfg, int epi, bool tc_bf16, bool nvfp4,
+                            int grid_y, hipStream_t s);
+
+// Re-tile bf16 [G][N][K] row-major weights into the MFMA lane order.
+hipError_t launch_retile_bf16(const bf16* src, bf16* dst, int G, int N, int K, hipStream_t s);
+
+// Unpermute + weighted reduce (+ shared + residual in direct mode).
+//   direct: out[t] = residual[t] + sum_j w[t][j] * y[inv[t*k+j]] + sh[t]
+//   latent: out[t] = sum_j w[t][j] * y[inv[t*k+j]]      (res, sh unused)
+hipError_t launch_unpermute_reduce(int out_dt, bool latent, const float* y, const int* inv,
+                                   const float* w, int n, int k, int D, const void* residual,
+                                   const float* sh, void* out, hipStream_t s);
+
+hipError_t launch_nvfp4_quantize(const float* w, int G, int rows, int cols, uint8_t* packed,
+                                 uint8_t* scales, float* scale2, hipStream_t s);

@@ -1,0 +1,541 @@
+// Host runtime of the MoE FFN layer: the C ABI declared in include/moe_layer.h.
+//
+// moe_layer_create (page "metrale_model_arch/nemotron_moe.rs",
+// `NemotronMoeLayer::new`: the config checks and the weight hand-off) copies
+// the weights into layer-owned HBM, re-tiling every bf16 projection into the
+// MFMA lane order, and allocates a workspace for max_tokens so that a forward
+// never allocates. moe_layer_forward (same page, `prefill`) enqueues:
+//
+//   norm_gate      RMSNorm + residual save + gate logits          (stream)
+//   shared up/down relu^2 FFN of the shared expert                (side stream)
+//   fc1            latent projection (LatentMoE only)             (stream)
+//   topk           sigmoid top-k + weights
+//   sort           histogram / prefix sum / stable scatter / tile list
+//   grouped up     gathered rows x up_e, relu^2 epilogue -> h (bf16)
+//   grouped down   h x down_e -> y (fp32, expert-sorted rows)
+//   reduce         direct: hidden = residual + sum_j w*y + shared
+//                  latent: o = sum_j w*y; fc2 GEMM with the residual and
+//                  shared added in its epilogue -> hidden
+//
+// The shared expert does not depend on routing, so it runs on a side stream
+// forked from the caller's stream by an event and joined before the reduce.
+// Nothing reads back to the host.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                                   \
+  do {                                                                                  \
+    hipError_t _e = (expr);                                                             \
+    if (_e != hipSuccess)                                                               \
+      return fail(MOE_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(_e));          \
+  } while (0)
+
+size_t dt_size(int dt) { return dt == MOE_DT_F32 ? 4 : 2; }
+
+}  // namespace
+
+struct moe_layer {
+  moe_layer_config_t cfg{};
+  int device = 0;
+  bool mfma = false;  // bf16 activations: MFMA kernels; fp32: SIMT kernels
+  // Weights (layer-owned).
+  void* gamma = nullptr;
+  void* gate = nullptr;
+  void* fc1 = nullptr;
+  void* fc2 = nullptr;
+  void* up = nullptr;
+  void* down = nullptr;
+  void* sh_up = nullptr;
+  void* sh_down = nullptr;
+  // Workspace (max_tokens rows).
+  void* normed = nullptr;
+  float* logits = nullptr;
+  int* ids = nullptr;
+  float* w = nullptr;
+  int* counts = nullptr;
+  int* offsets = nullptr;
+  int* perm = nullptr;
+  int* inv = nullptr;
+  int2* tiles = nullptr;
+  int* num_tiles = nullptr;
+  void* g_sh = nullptr;   // shared-expert activation [N][S]
+  float* sh = nullptr;    // shared-expert output fp32 [N][H]
+  void* z = nullptr;      // latent input [N][L]
+  void* h = nullptr;      // routed activation [R][I]
+  float* y = nullptr;     // routed output fp32 [R][D]
+  void* o = nullptr;      // latent routed sum [N][L]
+  std::vector<void*> allocs;
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  int last_n = 0;
+  // Stage timing: events[(fwd * MOE_NUM_STAGES + stage) * 2 + {0,1}].
+  bool timing = false;
+  uint32_t timing_mask = 0;
+  int timing_cap = 0, timing_count = 0;
+  std::vector<hipEvent_t> tev;
+  std::vector<uint8_t> trec;  // [fwd * MOE_NUM_STAGES + stage] recorded
+
+  int D() const { return cfg.latent_size > 0 ? cfg.latent_size : cfg.hidden_size; }
+};
+
+namespace {
+
+int dalloc(moe_layer* L, void** p, size_t bytes) {
+  *p = nullptr;
+  if (bytes == 0) return MOE_OK;
+  hipError_t e = hipMalloc(p, bytes);
+  if (e != hipSuccess) {
+    *p = nullptr;
+    (void)hipGetLastError();
+    return fail(MOE_ERR_OOM, "hipMalloc(%zu bytes) failed: %s", bytes, hipGetErrorString(e));
+  }
+  L->allocs.push_back(*p);
+  return MOE_OK;
+}
+
+void free_layer(moe_layer* L) {
+  if (!L) return;
+  for (void* p : L->allocs) (void)hipFree(p);
+  for (hipEvent_t e : L->tev) (void)hipEventDestroy(e);
+  if (L->ev_fork) (void)hipEventDestroy(L->ev_fork);
+  if (L->ev_join) (void)hipEventDestroy(L->ev_join);
+  if (L->side) (void)hipStreamDestroy(L->side);
+  delete L;
+}
+
+// Event pair around one stage of the current forward (no-op unless timing).
+struct StageScope {
+  moe_layer* L;
+  int stage;
+  hipStream_t s;
+  bool on;
+  StageScope(moe_layer* L_, int stage_, hipStream_t s_) : L(L_), stage(stage_), s(s_) {
+    on = L->timing && (L->timing_mask >> stage & 1u) && L->timing_count < L->timing_cap;
+    if (on) (void)hipEventRecord(L->tev[((size_t)L->timing_count * MOE_NUM_STAGES + stage) * 2], s);
+  }
+  ~StageScope() {
+    if (!on) return;
+    const size_t i = (size_t)L->timing_count * MOE_NUM_STAGES + stage;
+    (void)hipEventRecord(L->tev[i * 2 + 1], s);
+    L->trec[i] = 1;
+  }
+};
+
+int check_config(const moe_layer_config_t& c) {
+  if (c.num_experts < 1 || c.num_experts > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_INVALID_CONFIG, "num_experts=%d must be in 1..%d", c.num_experts,
+                MOE_MAX_EXPERTS);
+  if (c.top_k < 1 || c.top_k > c.num_experts || c.top_k > MOE_MAX_TOP_K)
+    return fail(MOE_ERR_INVALID_CONFIG,
+                "top_k=%d must be in 1..=%d and at most %d (routing bound)", c.top_k,
+                c.num_experts, MOE_MAX_TOP_K);
+  if (c.max_tokens < 1) return fail(MOE_ERR_INVALID_CONFIG, "max_tokens=%d < 1", c.max_tokens);
+  const bool f32 = c.act_dtype == MOE_DT_F32;
+  if (f32 && c.expert_dtype != MOE_DT_F32)
+    return fail(MOE_ERR_INVALID_CONFIG, "fp32 activations need fp32 experts");
+  if (c.act_dtype == MOE_DT_BF16 && c.expert_dtype != MOE_DT_BF16 &&
+      c.expert_dtype != MOE_DT_NVFP4)
+    return fail(MOE_ERR_INVALID_CONFIG, "bf16 activations need bf16 or NVFP4 experts");
+  if (c.act_dtype != MOE_DT_F32 && c.act_dtype != MOE_DT_BF16)
+    return fail(MOE_ERR_INVALID_CONFIG, "act_dtype=%d unsupported", c.act_dtype);
+  if (c.expert_dtype == MOE_DT_NVFP4)
+    return fail(MOE_ERR_INVALID_CONFIG, "NVFP4 experts are not built yet");
+  const int q = f32 ? 16 : 64;
+  const int dims[4] = {c.hidden_size, c.moe_inter, c.shared_inter, c.latent_size};
+  const char* names[4] = {"hidden_size", "moe_inter", "shared_inter", "latent_size"};
+  for (int i = 0; i < 4; ++i) {
+    const bool optional = i >= 2;
+    if (dims[i] < 0 || (!optional && dims[i] == 0) || dims[i] % q != 0)
+      return fail(MOE_ERR_INVALID_CONFIG, "%s=%d must be a %smultiple of %d", names[i], dims[i],
+                  optional ? "non-negative " : "positive ", q);
+  }
+  if (c.hidden_size > 8192)
+    return fail(MOE_ERR_INVALID_CONFIG, "hidden_size=%d exceeds 8192", c.hidden_size);
+  if (!(c.rms_eps >= 0.f)) return fail(MOE_ERR_INVALID_CONFIG, "rms_eps must be >= 0");
+  return MOE_OK;
+}
+
+// Copy a weight matrix stack [G][N][K] into layer memory: bf16 is re-tiled for
+// the MFMA kernels, fp32 is copied as is.
+int upload_proj(moe_layer* L, void** dst, const void* src, int G, int N, int K, bool retile,
+                hipStream_t s, const char* name) {
+  if (!src) return fail(MOE_ERR_INVALID_ARG, "weight '%s' is NULL", name);
+  const size_t elems = (size_t)G * N * K;
+  const size_t bytes = elems * (L->mfma ? 2 : 4);
+  int rc = dalloc(L, dst, bytes);
+  if (rc) return rc;
+  if (retile) {
+    HIP_TRY(launch_retile_bf16((const bf16*)src, (bf16*)*dst, G, N, K, s));
+  } else {
+    HIP_TRY(hipMemcpyAsync(*dst, src, bytes, hipMemcpyDeviceToDevice, s));
+  }
+  return MOE_OK;
+}
+
+MfmaCfg grouped_cfg(int rows_per_group) {
+  if (rows_per_group <= 16) return {16, 16};
+  if (rows_per_group <= 32) return {32, 32};
+  if (rows_per_group <= 80) return {32, 64};
+  return {32, 128};
+}
+
+MfmaCfg dense_cfg(int n) {
+  if (n <= 16) return {16, 16};
+  if (n <= 32) return {32, 32};
+  if (n <= 64) return {32, 64};
+  return {32, 128};
+}
+
+int gemm(moe_layer* L, const GemmArgs& a, int epi, bool out_bf16, int bm_or_cfg_rows,
+         MfmaCfg cfg, int grid_y, hipStream_t s, const char* what) {
+  hipError_t e;
+  if (L->mfma) {
+    e = launch_gemm_mfma(a, cfg, epi, out_bf16, false, grid_y, s);
+  } else {
+    (void)bm_or_cfg_rows;
+    e = launch_gemm_simt_f32(a, epi, grid_y, s);
+  }
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+int moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_weights_t* wts, void* stream,
+                     moe_layer_t** out) {
+  if (out) *out = nullptr;
+  if (!cfg || !wts || !out) return fail(MOE_ERR_INVALID_ARG, "NULL argument to moe_layer_create");
+  int rc = check_config(*cfg);
+  if (rc) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  moe_layer* L = new moe_layer();
+  L->cfg = *cfg;
+  L->mfma = cfg->act_dtype == MOE_DT_BF16;
+  const moe_layer_config_t& c = L->cfg;
+  const int H = c.hidden_size, E = c.num_experts, k = c.top_k, I = c.moe_inter,
+            S = c.shared_inter, Lt = c.latent_size, D = L->D(), N = c.max_tokens;
+  const size_t R = (size_t)N * k;
+  const size_t as = dt_size(c.act_dtype);
+
+#define TRY(x)            \
+  do {                    \
+    int _r = (x);         \
+    if (_r) {             \
+      free_layer(L);      \
+      return _r;          \
+    }                     \
+  } while (0)
+#define TRYH(x)                                                                        \
+  do {                                                                                 \
+    hipError_t _e = (x);                                                               \
+    if (_e != hipSuccess) {                                                            \
+      free_layer(L);                                                                   \
+      return fail(MOE_ERR_HIP, "%s failed: %s", #x, hipGetErrorString(_e));            \
+    }                                                                                  \
+  } while (0)
+
+  if (!wts->norm_gamma || !wts->gate || !wts->up || !wts->down ||
+      (S > 0 && (!wts->shared_up || !wts->shared_down))) {
+    free_layer(L);
+    return fail(MOE_ERR_INVALID_ARG, "a required weight (gamma, gate, up, down, shared) is NULL");
+  }
+  if (Lt > 0 && (!wts->fc1 || !wts->fc2)) {
+    free_layer(L);
+    return fail(MOE_ERR_INVALID_ARG, "latent layers need fc1 and fc2");
+  }
+  TRYH(hipGetDevice(&L->device));
+  // Weights.
+  TRY(dalloc(L, &L->gamma, H * as));
+  TRYH(hipMemcpyAsync(L->gamma, wts->norm_gamma, H * as, hipMemcpyDeviceToDevice, s));
+  TRY(dalloc(L, &L->gate, (size_t)E * H * as));
+  TRYH(hipMemcpyAsync(L->gate, wts->gate, (size_t)E * H * as, hipMemcpyDeviceToDevice, s));
+  if (Lt > 0) {
+    TRY(upload_proj(L, &L->fc1, wts->fc1, 1, Lt, H, L->mfma, s, "fc1"));
+    TRY(upload_proj(L, &L->fc2, wts->fc2, 1, H, Lt, L->mfma, s, "fc2"));
+  }
+  TRY(upload_proj(L, &L->up, wts->up, E, I, D, L->mfma, s, "up"));
+  TRY(upload_proj(L, &L->down, wts->down, E, D, I, L->mfma, s, "down"));
+  if (S > 0) {
+    TRY(upload_proj(L, &L->sh_up, wts->shared_up, 1, S, H, L->mfma, s, "shared_up"));
+    TRY(upload_proj(L, &L->sh_down, wts->shared_down, 1, H, S, L->mfma, s, "shared_down"));
+  }
+  // Workspace.
+  const size_t tiles_cap = R + (size_t)E + 1;  // >= sum_e ceil(c_e / bm) for any bm >= 1
+  TRY(dalloc(L, &L->normed, (size_t)N * H * as));
+  TRY(dalloc(L, (void**)&L->logits, (size_t)N * E * 4));
+  TRY(dalloc(L, (void**)&L->ids, R * 4));
+  TRY(dalloc(L, (void**)&L->w, R * 4));
+  TRY(dalloc(L, (void**)&L->counts, (size_t)E * 4));
+  TRY(dalloc(L, (void**)&L->offsets, (size_t)(E + 1) * 4));
+  TRY(dalloc(L, (void**)&L->perm, R * 4));
+  TRY(dalloc(L, (void**)&L->inv, R * 4));
+  TRY(dalloc(L, (void**)&L->tiles, tiles_cap * sizeof(int2)));
+  TRY(dalloc(L, (void**)&L->num_tiles, 16));
+  if (S > 0) {
+    TRY(dalloc(L, &L->g_sh, (size_t)N * S * as));
+    TRY(dalloc(L, (void**)&L->sh, (size_t)N * H * 4));
+  }
+  if (Lt > 0) {
+    TRY(dalloc(L, &L->z, (size_t)N * Lt * as));
+    TRY(dalloc(L, &L->o, (size_t)N * Lt * as));
+  }
+  TRY(dalloc(L, &L->h, R * I * as));
+  TRY(dalloc(L, (void**)&L->y, R * D * 4));
+
+  TRYH(hipStreamCreateWithFlags(&L->side, hipStreamNonBlocking));
+  TRYH(hipEventCreateWithFlags(&L->ev_fork, hipEventDisableTiming));
+  TRYH(hipEventCreateWithFlags(&L->ev_join, hipEventDisableTiming));
+  // The norm+gate kernel keeps TM=4 fp32 rows of hidden in LDS.
+  TRYH(hipStreamSynchronize(s));
+#undef TRY
+#undef TRYH
+  *out = L;
+  return MOE_OK;
+}
+
+void moe_layer_destroy(moe_layer_t* L) {
+  if (!L) return;
+  (void)hipDeviceSynchronize();
+  free_layer(L);
+}
+
+int moe_layer_forward(moe_layer_t* L, void* hidden, void* residual, int32_t n, void* stream) {
+  if (!L || !hidden || !residual) return fail(MOE_ERR_INVALID_ARG, "NULL argument to forward");
+  if (n < 0) return fail(MOE_ERR_INVALID_ARG, "num_tokens=%d < 0", n);
+  const moe_layer_config_t& c = L->cfg;
+  if (n > c.max_tokens)
+    return fail(MOE_ERR_TOO_MANY_TOKENS, "num_tokens=%d > max_tokens=%d", n, c.max_tokens);
+  if (n == 0) return MOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const int H = c.hidden_size, E = c.num_experts, k = c.top_k, I = c.moe_inter,
+            S = c.shared_inter, Lt = c.latent_size, D = L->D();
+  const int R = n * k;
+  const bool bf = L->mfma;
+  const MfmaCfg dc = dense_cfg(n);
+  const int dbmt = bf ? dc.bmt : 64;
+  const int dgrid = (n + dbmt - 1) / dbmt;
+
+  // 1. RMSNorm + residual + gate logits.
+  {
+    StageScope sc(L, MOE_STAGE_NORM_GATE, s);
+    HIP_TRY(launch_norm_gate(c.act_dtype, hidden, L->gamma, L->gate, L->normed, residual,
+                             L->logits, n, H, E, c.rms_eps, s));
+  }
+
+  // 2. Shared expert on the side stream.
+  if (S > 0) {
+    HIP_TRY(hipEventRecord(L->ev_fork, s));
+    HIP_TRY(hipStreamWaitEvent(L->side, L->ev_fork, 0));
+    {
+      StageScope sc(L, MOE_STAGE_SHARED_UP, L->side);
+      GemmArgs a{};
+      a.A = L->normed; a.lda = H; a.B = L->sh_up; a.C = L->g_sh; a.ldc = S;
+      a.M = n; a.N = S; a.K = H;
+      int rc = gemm(L, a, EPI_RELU2, bf, dbmt, dc, dgrid, L->side, "shared up");
+      if (rc) return rc;
+    }
+    {
+      StageScope sc(L, MOE_STAGE_SHARED_DOWN, L->side);
+      GemmArgs b{};
+      b.A = L->g_sh; b.lda = S; b.B = L->sh_down; b.C = L->sh; b.ldc = H;
+      b.M = n; b.N = H; b.K = S;
+      int rc = gemm(L, b, EPI_STORE, false, dbmt, dc, dgrid, L->side, "shared down");
+      if (rc) return rc;
+    }
+    HIP_TRY(hipEventRecord(L->ev_join, L->side));
+  }
+
+  // 3. Latent input.
+  const void* zin = L->normed;
+  if (Lt > 0) {
+    StageScope sc(L, MOE_STAGE_FC1, s);
+    GemmArgs a{};
+    a.A = L->normed; a.lda = H; a.B = L->fc1; a.C = L->z; a.ldc = Lt;
+    a.M = n; a.N = Lt; a.K = H;
+    int rc = gemm(L, a, EPI_STORE, bf, dbmt, dc, dgrid, s, "fc1");
+    if (rc) return rc;
+    zin = L->z;
+  }
+
+  // 4. Routing.
+  {
+    StageScope sc(L, MOE_STAGE_TOPK, s);
+    HIP_TRY(launch_topk(L->logits, n, E, k, c.routed_scaling_factor, L->ids, L->w, s));
+  }
+  const MfmaCfg gc = grouped_cfg((R + E - 1) / E);
+  const int bm = bf ? gc.bmt : 64;
+  {
+    StageScope sc(L, MOE_STAGE_SORT, s);
+    HIP_TRY(launch_route_sort(L->ids, R, E, L->counts, L->offsets, L->perm, L->inv, bm,
+                              L->tiles, L->num_tiles, s));
+  }
+  const int tiles_cap = (R + bm - 1) / bm + std::min(E, R);
+
+  // 5. Grouped expert GEMMs.
+  {
+    StageScope sc(L, MOE_STAGE_GROUPED_UP, s);
+    GemmArgs a{};
+    a.A = zin; a.lda = D; a.a_rows = L->perm; a.a_div = k;
+    a.B = L->up; a.b_gstride = (long long)I * D;
+    a.C = L->h; a.ldc = I; a.N = I; a.K = D;
+    a.tiles = L->tiles; a.num_tiles = L->num_tiles; a.offsets = L->offsets; a.bm = bm;
+    int rc = gemm(L, a, EPI_RELU2, bf, bm, gc, tiles_cap, s, "grouped up");
+    if (rc) return rc;
+  }
+  {
+    StageScope sc(L, MOE_STAGE_GROUPED_DOWN, s);
+    GemmArgs b{};
+    b.A = L->h; b.lda = I;
+    b.B = L->down; b.b_gstride = (long long)D * I;
+    b.C = L->y; b.ldc = D; b.N = D; b.K = I;
+    b.tiles = L->tiles; b.num_tiles = L->num_tiles; b.offsets = L->offsets; b.bm = bm;
+    int rc = gemm(L, b, EPI_STORE, false, bm, gc, tiles_cap, s, "grouped down");
+    if (rc) return rc;
+  }
+
+  // 6. Join the shared expert, reduce, residual.
+  if (S > 0) HIP_TRY(hipStreamWaitEvent(s, L->ev_join, 0));
+  if (Lt == 0) {
+    StageScope sc(L, MOE_STAGE_REDUCE, s);
+    HIP_TRY(launch_unpermute_reduce(c.act_dtype, false, L->y, L->inv, L->w, n, k, D, residual,
+                                    S > 0 ? L->sh : nullptr, hidden, s));
+  } else {
+    {
+      StageScope sc(L, MOE_STAGE_REDUCE, s);
+      HIP_TRY(launch_unpermute_reduce(c.act_dtype, true, L->y, L->inv, L->w, n, k, D, nullptr,
+                                      nullptr, L->o, s));
+    }
+    StageScope sc(L, MOE_STAGE_FC2, s);
+    GemmArgs a{};
+    a.A = L->o; a.lda = Lt; a.B = L->fc2; a.C = hidden; a.ldc = H;
+    a.M = n; a.N = H; a.K = Lt;
+    a.res = residual; a.add = S > 0 ? L->sh : nullptr;
+    int rc = gemm(L, a, EPI_ADD_RES, bf, dbmt, dc, dgrid, s, "fc2");
+    if (rc) return rc;
+  }
+  L->last_n = n;
+  if (L->timing && L->timing_count < L->timing_cap) L->timing_count++;
+  return MOE_OK;
+}
+
+int moe_layer_timing_begin(moe_layer_t* L, uint32_t mask, int32_t max_forwards) {
+  if (!L || max_forwards < 1 || max_forwards > 4096)
+    return fail(MOE_ERR_INVALID_ARG, "timing_begin needs a layer and 1..4096 forwards");
+  const size_t need = (size_t)max_forwards * MOE_NUM_STAGES * 2;
+  while (L->tev.size() < need) {
+    hipEvent_t e;
+    HIP_TRY(hipEventCreate(&e));
+    L->tev.push_back(e);
+  }
+  L->trec.assign((size_t)max_forwards * MOE_NUM_STAGES, 0);
+  L->timing_mask = mask;
+  L->timing_cap = max_forwards;
+  L->timing_count = 0;
+  L->timing = true;
+  return MOE_OK;
+}
+
+int moe_layer_timing_end(moe_layer_t* L, float* total_ms, int32_t* launches) {
+  if (!L || !total_ms || !launches) return fail(MOE_ERR_INVALID_ARG, "bad timing_end arguments");
+  L->timing = false;
+  for (int st = 0; st < MOE_NUM_STAGES; ++st) {
+    total_ms[st] = 0.f;
+    launches[st] = 0;
+  }
+  for (int f = 0; f < L->timing_count; ++f)
+    for (int st = 0; st < MOE_NUM_STAGES; ++st) {
+      const size_t i = (size_t)f * MOE_NUM_STAGES + st;
+      if (!L->trec[i]) continue;
+      HIP_TRY(hipEventSynchronize(L->tev[i * 2 + 1]));
+      float ms = 0.f;
+      HIP_TRY(hipEventElapsedTime(&ms, L->tev[i * 2], L->tev[i * 2 + 1]));
+      total_ms[st] += ms;
+      launches[st] += 1;
+    }
+  L->timing_count = 0;
+  return MOE_OK;
+}
+
+int moe_layer_debug_read(moe_layer_t* L, int32_t which, void* dst, int64_t bytes, void* stream) {
+  if (!L || !dst || bytes < 0) return fail(MOE_ERR_INVALID_ARG, "bad debug_read arguments");
+  const moe_layer_config_t& c = L->cfg;
+  const int64_t n = L->last_n, R = n * c.top_k;
+  const void* src = nullptr;
+  int64_t avail = 0;
+  switch (which) {
+    case MOE_DBG_NORMED: src = L->normed; avail = n * c.hidden_size * (int64_t)dt_size(c.act_dtype); break;
+    case MOE_DBG_LOGITS: src = L->logits; avail = n * c.num_experts * 4; break;
+    case MOE_DBG_IDS: src = L->ids; avail = R * 4; break;
+    case MOE_DBG_WEIGHTS: src = L->w; avail = R * 4; break;
+    case MOE_DBG_COUNTS: src = L->counts; avail = (int64_t)c.num_experts * 4; break;
+    case MOE_DBG_OFFSETS: src = L->offsets; avail = (int64_t)(c.num_experts + 1) * 4; break;
+    case MOE_DBG_PERM: src = L->perm; avail = R * 4; break;
+    case MOE_DBG_INV: src = L->inv; avail = R * 4; break;
+    default: return fail(MOE_ERR_INVALID_ARG, "unknown debug buffer %d", which);
+  }
+  if (n == 0 || bytes > avail)
+    return fail(MOE_ERR_INVALID_ARG, "debug_read of %lld bytes exceeds the %lld written",
+                (long long)bytes, (long long)avail);
+  HIP_TRY(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+int moe_topk_sigmoid(const float* logits, int32_t n, int32_t E, int32_t k, float scale,
+                     int32_t* ids, float* w, void* stream) {
+  if (n < 0 || (n > 0 && (!logits || !ids || !w)))
+    return fail(MOE_ERR_INVALID_ARG, "bad moe_topk_sigmoid arguments");
+  if (E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > E || k > MOE_MAX_TOP_K)
+    return fail(MOE_ERR_INVALID_CONFIG, "E=%d, k=%d outside the routing bounds", E, k);
+  if (n == 0) return MOE_OK;
+  HIP_TRY(launch_topk(logits, n, E, k, scale, ids, w, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+int moe_route_sort(const int32_t* ids, int32_t n, int32_t k, int32_t E, int32_t* counts,
+                   int32_t* offsets, int32_t* perm, int32_t* inv, void* stream) {
+  if (n < 0 || k < 1 || !counts || !offsets || (n > 0 && (!ids || !perm || !inv)))
+    return fail(MOE_ERR_INVALID_ARG, "bad moe_route_sort arguments");
+  if (E < 1 || E > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_INVALID_CONFIG, "E=%d outside 1..%d", E, MOE_MAX_EXPERTS);
+  HIP_TRY(launch_route_sort(ids, n * k, E, counts, offsets, perm, inv, 0, nullptr, nullptr,
+                            (hipStream_t)stream));
+  return MOE_OK;
+}
+
+int moe_nvfp4_quantize(const float* w, int32_t G, int32_t rows, int32_t cols, uint8_t* packed,
+                       uint8_t* scales, float* scale2, void* stream) {
+  if (G < 0 || rows < 0 || cols < 0 || cols % 16 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "bad shape (cols must be a multiple of 16)");
+  if ((size_t)G * rows * cols == 0) return MOE_OK;
+  if (!w || !packed || !scales || !scale2) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  HIP_TRY(launch_nvfp4_quantize(w, G, rows, cols, packed, scales, scale2, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+}  // extern "C"

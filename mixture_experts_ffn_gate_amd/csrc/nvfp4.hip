@@ -1,0 +1,119 @@
+// NVFP4 weight quantizer on the device (page "metrale_model_arch/nemotron_moe.rs":
+// NVFP4 weights are a packed 4-bit table, a per-block scale table and one
+// per-tensor scale2 per expert; the same page names a bf16 -> NVFP4 quantize
+// kernel). Two-level scheme, every step in fp32:
+//   scale2 = amax|W| / 2688             (2688 = 6 * 448)
+//   s_b    = E4M3_rne(amax_b / (6 * scale2))      per 16 consecutive K
+//   q      = E2M1_rne(w / (e4m3(s_b) * scale2))   saturating at 6
+// Round to nearest, ties to the even code; zero magnitudes keep the sign bit
+// clear; element k goes to byte k/2, low nibble when k is even.
+#include "kernels.h"
+
+// E4M3 ("fn": bias 7, no infinities, max 448) code of x >= 0, ties to even.
+__device__ __forceinline__ uint32_t e4m3_code_rne(float x) {
+  if (!(x > 0.f)) return 0u;
+  if (x >= 448.f) return 0x7Eu;
+  const uint32_t u = __float_as_uint(x);
+  const int e = (int)((u >> 23) & 0xFF) - 127;
+  if (e < -6) {
+    // Subnormal range: value = m * 2^-9; m = 8 is the smallest normal (code 8).
+    return (uint32_t)rintf(x * 512.0f);
+  }
+  // Round the fp32 mantissa to 3 bits (ties to even); a carry bumps the exponent.
+  const uint32_t lsb = (u >> 20) & 1u;
+  const uint32_t r = u + 0x7FFFFu + lsb;
+  const int eb = (int)((r >> 23) & 0xFF) - 127 + 7;
+  const uint32_t m = (r >> 20) & 7u;
+  if (eb > 15 || (eb == 15 && m == 7u)) return 0x7Eu;
+  return ((uint32_t)eb << 3) | m;
+}
+
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const int e = (c >> 3) & 15, m = c & 7;
+  return e == 0 ? ldexpf((float)m, -9) : ldexpf(1.0f + (float)m * 0.125f, e - 7);
+}
+
+// E2M1 code of v (magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6), ties to even code.
+__device__ __forceinline__ uint32_t e2m1_code_rne(float v) {
+  const float a = fabsf(v);
+  uint32_t m;
+  if (a <= 0.25f) m = 0;
+  else if (a < 0.75f) m = 1;
+  else if (a <= 1.25f) m = 2;
+  else if (a < 1.75f) m = 3;
+  else if (a <= 2.5f) m = 4;
+  else if (a < 3.5f) m = 5;
+  else if (a <= 5.0f) m = 6;
+  else m = 7;
+  if (m != 0 && v < 0.f) m |= 8u;
+  return m;
+}
+
+// amax of each matrix -> scale2[g] (one workgroup per matrix).
+__global__ void __launch_bounds__(256) nvfp4_scale2_kernel(const float* __restrict__ w,
+                                                           size_t per, float* __restrict__ scale2) {
+  __shared__ float red[4];
+  const float* src = w + (size_t)blockIdx.x * per;
+  float m = 0.f;
+  for (size_t i = threadIdx.x; i < per; i += 256) m = fmaxf(m, fabsf(src[i]));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    scale2[blockIdx.x] = a / 2688.0f;
+  }
+}
+
+// One thread per 16-element block: scale code + 8 packed bytes.
+__global__ void __launch_bounds__(256) nvfp4_pack_kernel(const float* __restrict__ w, int G,
+                                                         int rows, int cols,
+                                                         const float* __restrict__ scale2,
+                                                         uint8_t* __restrict__ packed,
+                                                         uint8_t* __restrict__ scales) {
+  const size_t nb_per = (size_t)rows * (cols / 16);
+  const size_t total = nb_per * G;
+  for (size_t b = blockIdx.x * (size_t)blockDim.x + threadIdx.x; b < total;
+       b += (size_t)gridDim.x * blockDim.x) {
+    const int g = (int)(b / nb_per);
+    const float s2 = scale2[g];
+    const float* src = w + b * 16;
+    float v[16];
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      v[i] = src[i];
+      amax = fmaxf(amax, fabsf(v[i]));
+    }
+    uint32_t sc = 0;
+    float denom = 0.f;
+    if (s2 > 0.f) {
+      const float t = 6.0f * s2;
+      sc = e4m3_code_rne(amax / t);
+      denom = e4m3_value(sc) * s2;
+    }
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t q = denom > 0.f ? e2m1_code_rne(v[i] / denom) : 0u;
+      if (i < 8) lo |= q << (4 * i);
+      else hi |= q << (4 * (i - 8));
+    }
+    *(u32x2*)(packed + b * 8) = u32x2{lo, hi};
+    scales[b] = (uint8_t)sc;
+  }
+}
+
+hipError_t launch_nvfp4_quantize(const float* w, int G, int rows, int cols, uint8_t* packed,
+                                 uint8_t* scales, float* scale2, hipStream_t s) {
+  const size_t per = (size_t)rows * cols;
+  hipLaunchKernelGGL(nvfp4_scale2_kernel, dim3(G), dim3(256), 0, s, w, per, scale2);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t total = (size_t)G * rows * (cols / 16);
+  const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
+  hipLaunchKernelGGL(nvfp4_pack_kernel, dim3(blocks), dim3(256), 0, s, w, G, rows, cols, scale2,
+                     packed, scales);
+  return hipGetLastError();
+}

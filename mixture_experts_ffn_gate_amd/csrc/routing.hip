@@ -1,0 +1,316 @@
+// Routing front end of the MoE layer on gfx950:
+//   norm_gate_kernel   RMSNorm (+ residual save) fused with the gate projection
+//   topk_sigmoid_kernel  wave64 sigmoid top-k with renormalized weights
+//   route_sort_kernel  per-expert histogram, prefix sum and stable scatter,
+//                      plus the (expert, row-block) tile list of the grouped GEMMs
+//
+// Sources: page "metrale_model_arch/nemotron_moe.rs" (module doc: forward
+// order RMS norm -> gate -> sigmoid top-k; `prefill`: rms_norm_residual,
+// gate GEMM, scratch carve-out of ids and weights); page "Struct MoeLayer"
+// (`forward_prefill`: sort-by-expert before the grouped GEMMs; `forward`:
+// routing stays on the device; `fp32_routing_active`: router input at full
+// precision).
+#include "kernels.h"
+
+// ---------------------------------------------------------------------------
+// Fused RMSNorm + gate.
+// Block = 256 threads (4 waves) handles TM tokens and experts
+// [blockIdx.y * epb, min(E, (blockIdx.y + 1) * epb)).
+//   1. sum of squares of each token row (one wave per token, TM <= 4 here)
+//   2. normed rows in fp32 -> LDS; blockIdx.y == 0 also writes `normed` in the
+//      activation dtype and `residual = hidden`
+//   3. logits[t][e] = sum_i W_g[e][i] * n_f32[t][i]: lanes split the hidden
+//      dimension in 8-element chunks, waves take experts in turn, and each
+//      expert's partial sums end in a wave reduction.
+// The gate reads the fp32 normed values, never the rounded copy, so the top-k
+// decision sees full-precision logits.
+// ---------------------------------------------------------------------------
+template <typename TA, int TM>
+__global__ void __launch_bounds__(256) norm_gate_kernel(const TA* __restrict__ hidden,
+                                                        const TA* __restrict__ gamma,
+                                                        const TA* __restrict__ wgate,
+                                                        TA* __restrict__ normed,
+                                                        TA* __restrict__ residual,
+                                                        float* __restrict__ logits, int n,
+                                                        int H, int E, int epb, float eps) {
+  extern __shared__ float nsh[];  // [TM][H] fp32 normed rows
+  __shared__ float rinv[TM];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * TM;
+  const int tcount = min(TM, n - t0);
+
+  // 1. inverse RMS per token
+  for (int t = wave; t < TM; t += 4) {
+    float ss = 0.f;
+    if (t < tcount) {
+      const TA* x = hidden + (size_t)(t0 + t) * H;
+      for (int i = lane; i < H; i += 64) {
+        float v = io<TA>::ld(x + i);
+        ss += v * v;
+      }
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) rinv[t] = 1.0f / sqrtf(ss / (float)H + eps);
+  }
+  __syncthreads();
+
+  // 2. normed rows
+  const bool writer = blockIdx.y == 0;
+  for (int idx = threadIdx.x; idx < TM * H; idx += 256) {
+    int t = idx / H, i = idx - t * H;
+    float v = 0.f;
+    if (t < tcount) {
+      size_t g = (size_t)(t0 + t) * H + i;
+      float x = io<TA>::ld(hidden + g);
+      v = x * rinv[t] * io<TA>::ld(gamma + i);
+      if (writer) {
+        io<TA>::st(residual + g, x);
+        io<TA>::st(normed + g, v);
+      }
+    }
+    nsh[idx] = v;
+  }
+  __syncthreads();
+
+  // 3. gate logits
+  const int e_begin = blockIdx.y * epb;
+  const int e_end = min(E, e_begin + epb);
+  for (int e = e_begin + wave; e < e_end; e += 4) {
+    float acc[TM];
+#pragma unroll
+    for (int t = 0; t < TM; ++t) acc[t] = 0.f;
+    const TA* wrow = wgate + (size_t)e * H;
+    for (int i0 = lane * 8; i0 < H; i0 += 512) {
+      float wv[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) wv[q] = io<TA>::ld(wrow + i0 + q);
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
+        const float* nr = nsh + t * H + i0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[t] += wv[q] * nr[q];
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+      float s = wave_sum(acc[t]);
+      if (lane == 0 && t < tcount) logits[(size_t)(t0 + t) * E + e] = s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Sigmoid top-k. One wave64 per token; lane l holds experts l, l+64, ...
+// Selection key = (fp32 bits of the score) << 32 | (0xFFFFFFFF - e): scores
+// lie in [0, 1], so their bit patterns order like the values, and among equal
+// scores the lower expert index has the larger key. k rounds of a wave-wide
+// 64-bit max reduction pick the experts in slot order (score desc, index asc).
+// ---------------------------------------------------------------------------
+template <int EPL>
+__global__ void __launch_bounds__(256) topk_sigmoid_kernel(const float* __restrict__ logits,
+                                                           int n, int E, int k, float scale,
+                                                           int* __restrict__ ids,
+                                                           float* __restrict__ wout) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= n) return;
+  uint64_t key[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    int e = lane + 64 * i;
+    key[i] = 0;
+    if (e < E) {
+      float l = logits[(size_t)t * E + e];
+      float s = 1.0f / (1.0f + expf(-l));
+      key[i] = ((uint64_t)__float_as_uint(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+    }
+  }
+  int my_e = 0;
+  float my_s = 0.f, sum = 0.f;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) best = key[i] > best ? key[i] : best;
+    best = wave_max_u64(best);
+    const int e = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
+    const float s = __uint_as_float((uint32_t)(best >> 32));
+    sum += s;
+    if (lane == j) { my_e = e; my_s = s; }
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (lane + 64 * i == e) key[i] = 0;
+  }
+  if (lane < k) {
+    float wv = sum > 0.f ? my_s / sum : 1.0f / (float)k;
+    ids[(size_t)t * k + lane] = my_e;
+    wout[(size_t)t * k + lane] = wv * scale;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Stable route sort in one workgroup of 1024 threads (16 waves).
+//   phase 1: per-expert histogram (LDS atomics: counts do not depend on order)
+//   phase 2: exclusive prefix sum -> offsets; tile list of ceil(count/bm)
+//            (expert, first local row) pairs per expert
+//   phase 3: routes in chunks of 1024, in order. Inside a wave, the lanes
+//            holding the same expert are found with one ballot per id bit;
+//            a lane's rank is the number of such lanes below it. Waves add the
+//            counts of lower waves in the same chunk, and the chunk adds the
+//            running base of its expert. So positions ascend with the route id
+//            within an expert: the order is stable and deterministic.
+// Ids outside [0, E) are skipped (they get no position).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(1024) route_sort_kernel(const int* __restrict__ ids, int R,
+                                                          int E, int* __restrict__ counts,
+                                                          int* __restrict__ offsets,
+                                                          int* __restrict__ perm,
+                                                          int* __restrict__ inv, int bm,
+                                                          int2* __restrict__ tiles,
+                                                          int* __restrict__ num_tiles) {
+  __shared__ int cnt[MOE_MAX_E];
+  __shared__ int base[MOE_MAX_E];
+  __shared__ int tbase[MOE_MAX_E];
+  __shared__ int wcnt[16][MOE_MAX_E];
+  __shared__ int scan_tmp[2][1024];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  for (int e = tid; e < MOE_MAX_E; e += 1024) {
+    cnt[e] = 0;
+    for (int w = 0; w < 16; ++w) wcnt[w][e] = 0;
+  }
+  __syncthreads();
+  for (int r = tid; r < R; r += 1024) {
+    int e = ids[r];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+
+  // Exclusive scans over experts of counts and of tile counts (E <= 512 < 1024).
+  int c = tid < E ? cnt[tid] : 0;
+  int tc = (tid < E && bm > 0) ? (c + bm - 1) / bm : 0;
+  scan_tmp[0][tid] = c;
+  scan_tmp[1][tid] = tc;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    int a = tid >= off ? scan_tmp[0][tid - off] : 0;
+    int b = tid >= off ? scan_tmp[1][tid - off] : 0;
+    __syncthreads();
+    scan_tmp[0][tid] += a;
+    scan_tmp[1][tid] += b;
+    __syncthreads();
+  }
+  if (tid < E) {
+    int excl = scan_tmp[0][tid] - c;
+    int texcl = scan_tmp[1][tid] - tc;
+    base[tid] = excl;
+    tbase[tid] = texcl;
+    counts[tid] = c;
+    offsets[tid] = excl;
+    if (tid == E - 1) {
+      offsets[E] = scan_tmp[0][tid];
+      if (num_tiles) *num_tiles = scan_tmp[1][tid];
+    }
+    if (tiles)
+      for (int i = 0; i < tc; ++i) tiles[texcl + i] = make_int2(tid, i * bm);
+  }
+  __syncthreads();
+
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int c0 = 0; c0 < R; c0 += 1024) {
+    const int r = c0 + tid;
+    int e = r < R ? ids[r] : -1;
+    const bool valid = e >= 0 && e < E;
+    if (!valid) e = -1;
+    uint64_t mask = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 10; ++b) {  // 10 bits cover E <= 1024
+      const bool bit = valid && ((e >> b) & 1);
+      const uint64_t bal = __ballot(bit);
+      mask &= bit ? bal : ~bal;
+    }
+    const int rank = __popcll(mask & below);
+    if (valid && rank == 0) wcnt[wave][e] = __popcll(mask);
+    __syncthreads();
+    if (valid) {
+      int pre = 0;
+      for (int w = 0; w < wave; ++w) pre += wcnt[w][e];
+      const int pos = base[e] + pre + rank;
+      perm[pos] = r;
+      inv[r] = pos;
+    }
+    __syncthreads();
+    for (int ee = tid; ee < E; ee += 1024) {
+      int s = 0;
+      for (int w = 0; w < 16; ++w) {
+        s += wcnt[w][ee];
+        wcnt[w][ee] = 0;
+      }
+      base[ee] += s;
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+template <int TM>
+static void norm_gate_tm(int act_dt, const void* hidden, const void* gamma, const void* wgate,
+                         void* normed, void* residual, float* logits, int n, int H, int E,
+                         float eps, hipStream_t s) {
+  const int bx = (n + TM - 1) / TM;
+  int ysplit = 1;
+  // Small batches: spread the experts over more workgroups (at least 4 per block).
+  while (bx * ysplit < 256 && E / (ysplit * 2) >= 4) ysplit *= 2;
+  const int epb = (E + ysplit - 1) / ysplit;
+  const size_t lds = (size_t)TM * H * sizeof(float);
+  dim3 grid(bx, ysplit);
+  if (act_dt == MOE_DT_BF16) {
+    hipLaunchKernelGGL((norm_gate_kernel<bf16, TM>), grid, dim3(256), lds, s,
+                       (const bf16*)hidden, (const bf16*)gamma, (const bf16*)wgate,
+                       (bf16*)normed, (bf16*)residual, logits, n, H, E, epb, eps);
+  } else {
+    hipLaunchKernelGGL((norm_gate_kernel<float, TM>), grid, dim3(256), lds, s,
+                       (const float*)hidden, (const float*)gamma, (const float*)wgate,
+                       (float*)normed, (float*)residual, logits, n, H, E, epb, eps);
+  }
+}
+
+hipError_t launch_norm_gate(int act_dt, const void* hidden, const void* gamma, const void* wgate,
+                            void* normed, void* residual, float* logits, int n, int H, int E,
+                            float eps, hipStream_t s) {
+  // TM fp32 rows of H stay in LDS; keep them within 60 KiB.
+  if (H * 4 * 4 <= 60 * 1024)
+    norm_gate_tm<4>(act_dt, hidden, gamma, wgate, normed, residual, logits, n, H, E, eps, s);
+  else if (H * 2 * 4 <= 60 * 1024)
+    norm_gate_tm<2>(act_dt, hidden, gamma, wgate, normed, residual, logits, n, H, E, eps, s);
+  else
+    norm_gate_tm<1>(act_dt, hidden, gamma, wgate, normed, residual, logits, n, H, E, eps, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const float* logits, int n, int E, int k, float scale, int* ids, float* w,
+                       hipStream_t s) {
+  dim3 grid((n + 3) / 4);
+  const int epl = (E + 63) / 64;
+  switch (epl) {
+#define TOPK_CASE(X)                                                                         \
+  case X:                                                                                    \
+    hipLaunchKernelGGL((topk_sigmoid_kernel<X>), grid, dim3(256), 0, s, logits, n, E, k, scale, \
+                       ids, w);                                                              \
+    break;
+    TOPK_CASE(1) TOPK_CASE(2) TOPK_CASE(3) TOPK_CASE(4) TOPK_CASE(5) TOPK_CASE(6) TOPK_CASE(7)
+    TOPK_CASE(8)
+#undef TOPK_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_route_sort(const int* ids, int R, int E, int* counts, int* offsets, int* perm,
+                             int* inv, int bm, int2* tiles, int* num_tiles, hipStream_t s) {
+  hipLaunchKernelGGL(route_sort_kernel, dim3(1), dim3(1024), 0, s, ids, R, E, counts, offsets,
+                     perm, inv, bm, tiles, num_tiles);
+  return hipGetLastError();
+}

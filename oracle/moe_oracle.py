@@ -47,6 +47,7 @@ Pins (tests that tie each function to something other than itself):
   rms_norm          closed form on constant rows; exact rational brute force
   gate_logits       one-hot gate rows select normed entries; brute force loop
   sigmoid_scores    closed values (0 -> 0.5, symmetric pairs sum to 1)
+  rank_margin       brute force over sorted score lists
   topk_select       brute force over all k-subsets / Python ``sorted`` with an
                     explicit key, forced ties
   routing_weights   sum to scale; all-equal scores give 1/k
@@ -134,6 +135,22 @@ def topk_select(scores, k: int):
     else:
         margin = np.full(n, np.inf)
     return ids, margin
+
+
+def rank_margin(scores, k: int):
+    """Smallest gap between adjacent ranks among a token's top ``k+1`` scores.
+
+    A token whose rank margin is small can legally change its selected set or
+    its slot order under a different rounding of the logits; the parity tests
+    compare ids exactly only where this margin is at least their threshold.
+    (With k == E the top k are all experts and only their order matters.)
+    """
+    s = np.asarray(scores).astype(F64)
+    n, e = s.shape
+    ranked = -np.sort(-s, axis=-1)[:, :min(k + 1, e)]
+    if ranked.shape[1] < 2:
+        return np.full(n, np.inf)
+    return np.min(ranked[:, :-1] - ranked[:, 1:], axis=-1)
 
 
 def routing_weights(scores, ids, scale: float = 1.0):

@@ -1,0 +1,88 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before touching the GPU (no compute calls here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_layer.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(moe_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def mod():
+    from mixture_experts_ffn_gate_amd import moe_layer
+    return moe_layer
+
+
+def test_header_declares_the_binding_exports(mod):
+    assert _declared_functions() == sorted(mod.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(mod):
+    lib = ctypes.CDLL(mod.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_struct_layouts_match_header(mod):
+    # 7 int32 + 2 float + 2 int32, no padding.
+    assert ctypes.sizeof(mod.Config) == 11 * 4
+    # 8 pointers + 4 NVFP4 triplets of pointers.
+    assert ctypes.sizeof(mod.Weights) == (8 + 12) * ctypes.sizeof(ctypes.c_void_p)
+
+
+def _cfg(mod, **kw):
+    base = dict(hidden_size=256, num_experts=8, top_k=2, moe_inter=128, shared_inter=256,
+                latent_size=0, max_tokens=64, rms_eps=1e-5, routed_scaling_factor=1.0,
+                act_dtype=mod.MOE_DT_BF16, expert_dtype=mod.MOE_DT_BF16)
+    base.update(kw)
+    return mod.Config(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(top_k=0), -2), (dict(top_k=9), -2), (dict(num_experts=600, top_k=2), -2),
+    (dict(num_experts=32, top_k=17), -2), (dict(hidden_size=100), -2),
+    (dict(moe_inter=96), -2), (dict(max_tokens=0), -2),
+    (dict(act_dtype=0, expert_dtype=1), -2), (dict(act_dtype=7), -2),
+    (dict(shared_inter=-64), -2), (dict(hidden_size=16384), -2),
+])
+def test_create_rejects_bad_config_on_host(mod, kw, code):
+    lib = mod.lib()
+    cfg = _cfg(mod, **kw)
+    w = mod.Weights()
+    out = ctypes.c_void_p(123)
+    rc = lib.moe_layer_create(ctypes.byref(cfg), ctypes.byref(w), None, ctypes.byref(out))
+    assert rc == code
+    assert out.value is None
+    assert lib.moe_last_error().decode()
+
+
+def test_null_arguments_rejected(mod):
+    lib = mod.lib()
+    out = ctypes.c_void_p()
+    assert lib.moe_layer_create(None, None, None, ctypes.byref(out)) == -1
+    assert lib.moe_layer_forward(None, None, None, 4, None) == -1
+    assert lib.moe_topk_sigmoid(None, 4, 8, 2, 1.0, None, None, None) == -1
+    assert lib.moe_topk_sigmoid(None, 0, 8, 9, 1.0, None, None, None) == -2
+    assert lib.moe_route_sort(None, 4, 2, 8, None, None, None, None, None) == -1
+    assert lib.moe_nvfp4_quantize(None, 1, 4, 20, None, None, None, None) == -1
+    assert lib.moe_layer_debug_read(None, 0, None, 0, None) == -1
+    lib.moe_layer_destroy(None)   # no-op
+
+
+def test_fp32_layers_accept_multiples_of_16(mod):
+    lib = mod.lib()
+    cfg = _cfg(mod, act_dtype=0, expert_dtype=0, hidden_size=48, moe_inter=96)
+    w = mod.Weights()   # all NULL: fails on the missing weights, after the config passed
+    out = ctypes.c_void_p()
+    rc = lib.moe_layer_create(ctypes.byref(cfg), ctypes.byref(w), None, ctypes.byref(out))
+    assert rc in (-1, -5)  # -5 only where no HIP device can be queried

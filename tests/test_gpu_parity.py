@@ -1,0 +1,277 @@
+"""GPU parity of the HIP path against the float64 oracle (through the C ABI).
+
+Bars: sort stage and quantizer bit-exact; top-k ids exact wherever the
+oracle's rank margin is >= 1e-3; layer outputs within relative Frobenius
+1e-4 (fp32), 1e-2 (bf16), 3e-2 (NVFP4) on both hidden_out and the MoE delta
+hidden_out - residual.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_ffn_gate_amd import workloads as wlm
+from oracle import moe_oracle as mo
+from oracle import nvfp4 as onv
+
+import parity_utils as pu
+
+pytestmark = pytest.mark.gpu
+f32np = wlm.to_numpy_f32
+
+
+@pytest.fixture(scope="module")
+def ml():
+    from mixture_experts_ffn_gate_amd import moe_layer
+    torch.cuda.init()
+    return moe_layer
+
+
+def _announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def run_layer(ml, wl, n, seed=0, W=None, hidden=None, max_tokens=None):
+    _announce(f"{wl.name} H={wl.H} E={wl.E} k={wl.k} I={wl.I} S={wl.S} L={wl.L} N={n} seed={seed}")
+    if W is None:
+        W = wlm.make_weights(wl, seed, "cuda")
+    if hidden is None:
+        hidden, residual = wlm.make_hidden(wl, n, seed, "cuda", gate=W["gate"])
+    else:
+        residual = torch.randn_like(hidden)
+    x = f32np(hidden)
+    layer = ml.layer_from_workload(wl, W, max_tokens=max_tokens or n)
+    layer.forward(hidden, residual)
+    ids = torch.empty(n, wl.k, dtype=torch.int32, device="cuda")
+    layer.debug_read("ids", ids)
+    torch.cuda.synchronize()
+    return dict(layer=layer, W=W, x=x, out=f32np(hidden), res=f32np(residual),
+                ids=ids.cpu().numpy(), hidden=hidden, residual=residual)
+
+
+# ------------------------------------------------------------------ stages --
+
+@pytest.mark.parametrize("n,E,k,ties", [(1000, 128, 6, False), (257, 8, 2, False),
+                                        (300, 512, 16, False), (123, 200, 7, False),
+                                        (500, 64, 4, True), (64, 16, 16, True)])
+def test_topk_stage(ml, n, E, k, ties):
+    _announce(f"topk n={n} E={E} k={k} ties={ties}")
+    g = torch.Generator().manual_seed(n * 7 + E)
+    logits = torch.randn(n, E, generator=g)
+    if ties:
+        logits = torch.round(logits * 2) / 2
+    ids, w = ml.topk_sigmoid(logits.cuda(), k, scale=1.0)
+    ids, w = ids.cpu().numpy(), w.cpu().numpy()
+    scores = mo.sigmoid_scores(logits.numpy())
+    ref_ids, _ = mo.topk_select(scores, k)
+    margin = mo.rank_margin(scores, k)
+    pu.check_ids(ids, ref_ids, margin, max_loose_frac=1.0 if ties else 0.05)
+    same = np.all(ids == ref_ids, axis=1)
+    ref_w = mo.routing_weights(scores, ref_ids, 1.0)
+    np.testing.assert_allclose(w[same], ref_w[same], rtol=2e-6, atol=1e-7)
+    np.testing.assert_allclose(w.sum(1), 1.0, rtol=1e-5)
+    if ties:
+        # Exact ties in fp32 scores: both sides break them by the lower index.
+        exact = np.all(ids == ref_ids, axis=1).mean()
+        assert exact > 0.99
+
+
+def test_topk_scale_and_ties_lowest_index(ml):
+    logits = torch.zeros(5, 32)
+    ids, w = ml.topk_sigmoid(logits.cuda(), 4, scale=2.5)
+    assert (ids.cpu().numpy() == np.arange(4)).all()
+    np.testing.assert_allclose(w.cpu().numpy(), 2.5 / 4, rtol=1e-6)
+
+
+@pytest.mark.parametrize("n,k,E,mode", [(1024, 6, 128, "uniform"), (4096, 6, 128, "uniform"),
+                                        (77, 4, 16, "uniform"), (3000, 8, 128, "one"),
+                                        (513, 2, 512, "sparse"), (1, 1, 8, "uniform"),
+                                        (2048, 16, 64, "uniform")])
+def test_route_sort_stage_bit_exact(ml, n, k, E, mode):
+    _announce(f"route_sort n={n} k={k} E={E} mode={mode}")
+    rng = np.random.default_rng(n + k + E)
+    if mode == "one":
+        # Every token routes to expert 0 plus k-1 experts drawn from a few.
+        ids = np.stack([np.concatenate([[0], rng.choice(np.arange(1, k + 3), k - 1,
+                                                        replace=False)]) for _ in range(n)])
+    elif mode == "sparse":
+        ids = np.stack([rng.choice(np.arange(0, E, 37), k, replace=False) for _ in range(n)])
+    else:
+        ids = np.stack([rng.choice(E, k, replace=False) for _ in range(n)])
+    ids = ids.astype(np.int32)
+    c, o, p, i = ml.route_sort(torch.from_numpy(ids).cuda(), E)
+    rc, ro, rp, ri = mo.sort_routes(ids, E)
+    np.testing.assert_array_equal(c.cpu().numpy(), rc)
+    np.testing.assert_array_equal(o.cpu().numpy(), ro)
+    np.testing.assert_array_equal(p.cpu().numpy(), rp)
+    np.testing.assert_array_equal(i.cpu().numpy(), ri)
+
+
+@pytest.mark.parametrize("G,rows,cols", [(3, 64, 256), (2, 48, 2688), (1, 16, 16)])
+def test_nvfp4_quantize_stage_bit_exact(ml, G, rows, cols):
+    _announce(f"nvfp4_quantize G={G} rows={rows} cols={cols}")
+    g = torch.Generator().manual_seed(G * rows + cols)
+    w = torch.randn(G, rows, cols, generator=g) / np.sqrt(cols)
+    # Exact E2M1 / E4M3 rounding ties: a block whose entries land on midpoints.
+    w[0, 0, :16] = torch.tensor([6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0,
+                                 -0.25, -0.75, -2.5, -5.0, 0.0, -0.0, 4.0, -6.0]) * 0.01
+    if G > 1:
+        w[1, 1] = 0.0
+    packed, scales, scale2 = ml.nvfp4_quantize(w.cuda())
+    rp, rs, r2 = onv.quantize_stack(w.numpy())
+    np.testing.assert_array_equal(scale2.cpu().numpy(), r2)
+    np.testing.assert_array_equal(scales.cpu().numpy(), rs)
+    np.testing.assert_array_equal(packed.cpu().numpy(), rp)
+
+
+# ------------------------------------------------------------- whole layer --
+
+SMALL = {
+    "direct_ragged": wlm.Workload("direct_ragged", H=512, E=16, k=4, I=192, S=320, L=0, N=77),
+    "latent_ragged": wlm.Workload("latent_ragged", H=512, E=16, k=4, I=256, S=320, L=192, N=130),
+    "no_shared": wlm.Workload("no_shared", H=256, E=8, k=2, I=128, S=0, L=0, N=200),
+    "topk_all": wlm.Workload("topk_all", H=256, E=8, k=8, I=64, S=64, L=0, N=40),
+    "many_rows": wlm.Workload("many_rows", H=256, E=4, k=2, I=128, S=128, L=0, N=700),
+}
+
+
+def test_tiny_f32_full(ml):
+    wl = wlm.WORKLOADS["tiny_direct_f32"]
+    r = run_layer(ml, wl, wl.N)
+    Wn = pu.oracle_weights(r["W"])
+    e = pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"])
+    print("errors", e)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_bf16(ml, name):
+    wl = SMALL[name]
+    r = run_layer(ml, wl, wl.N, seed=5)
+    Wn = pu.oracle_weights(r["W"])
+    print("errors", pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"]))
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 16, 17, 64])
+def test_small_bf16_token_counts(ml, n):
+    wl = SMALL["direct_ragged"]
+    r = run_layer(ml, wl, n, seed=11, max_tokens=128)
+    Wn = pu.oracle_weights(r["W"])
+    pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"])
+
+
+def test_skewed_routing_many_row_blocks(ml):
+    # Nearly identical rows route to the same experts: one expert gets every
+    # token, so its rows span several row blocks of the grouped GEMMs.
+    wl = wlm.Workload("skewed", H=256, E=8, k=2, I=128, S=64, L=0, N=600)
+    W = wlm.make_weights(wl, 3, "cuda")
+    base = torch.randn(1, wl.H, device="cuda")
+    hidden = (base + 0.05 * torch.randn(wl.N, wl.H, device="cuda")).to(torch.bfloat16)
+    r = run_layer(ml, wl, wl.N, W=W, hidden=hidden)
+    assert np.bincount(r["ids"].ravel(), minlength=wl.E).max() > 300
+    Wn = pu.oracle_weights(W)
+    pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"])
+
+
+def test_sort_stage_bit_exact_inside_forward(ml):
+    wl = SMALL["direct_ragged"]
+    r = run_layer(ml, wl, wl.N, seed=2)
+    L = r["layer"]
+    R = wl.N * wl.k
+    bufs = {nm: torch.empty(sz, dtype=torch.int32, device="cuda")
+            for nm, sz in (("counts", wl.E), ("offsets", wl.E + 1), ("perm", R), ("inv", R))}
+    for nm, t in bufs.items():
+        L.debug_read(nm, t)
+    torch.cuda.synchronize()
+    rc, ro, rp, ri = mo.sort_routes(r["ids"], wl.E)
+    for nm, ref in zip(("counts", "offsets", "perm", "inv"), (rc, ro, rp, ri)):
+        np.testing.assert_array_equal(bufs[nm].cpu().numpy(), ref, err_msg=nm)
+
+
+def test_residual_input_ignored_and_deterministic(ml):
+    wl = SMALL["direct_ragged"]
+    W = wlm.make_weights(wl, 4, "cuda")
+    h0, _ = wlm.make_hidden(wl, wl.N, 4, "cuda")
+    layer = ml.layer_from_workload(wl, W)
+    outs = []
+    for garbage in (0.0, 1e30):
+        h = h0.clone()
+        res = torch.full_like(h, garbage)
+        layer.forward(h, res)
+        outs.append((h.clone(), res.clone()))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert torch.equal(outs[0][1], h0) and torch.equal(outs[1][1], h0)
+
+
+def test_errors_and_zero_tokens(ml):
+    wl = SMALL["no_shared"]
+    W = wlm.make_weights(wl, 0, "cuda")
+    layer = ml.layer_from_workload(wl, W, max_tokens=8)
+    h = torch.randn(9, wl.H, device="cuda").to(torch.bfloat16)
+    r = torch.empty_like(h)
+    with pytest.raises(ml.MoeError) as ei:
+        layer.forward(h, r)
+    assert ei.value.code == ml.MOE_ERR_TOO_MANY_TOKENS
+    h2 = h[:4].clone()
+    layer.forward(h2, r[:4].contiguous(), num_tokens=0)
+    torch.cuda.synchronize()
+    assert torch.equal(h2, h[:4])
+
+
+def test_graph_capture_replays_match_eager(ml):
+    # A forward enqueues no host synchronization, allocation or readback, so
+    # it can be captured; replays (with eager work between them) must match.
+    wl = SMALL["latent_ragged"]
+    W = wlm.make_weights(wl, 6, "cuda")
+    h0, _ = wlm.make_hidden(wl, wl.N, 6, "cuda")
+    layer = ml.layer_from_workload(wl, W)
+    eager = h0.clone()
+    res = torch.empty_like(eager)
+    layer.forward(eager, res)
+    torch.cuda.synchronize()
+    hbuf = h0.clone()
+    rbuf = torch.empty_like(hbuf)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            layer.forward(hbuf, rbuf, stream=s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        hbuf.copy_(h0)
+        junk = torch.randn(1000, device="cuda").sum()  # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(hbuf, eager), f"replay {rep}"
+        assert torch.equal(rbuf, h0)
+        del junk
+
+
+# ------------------------------------------------ full sizes (bench shapes) --
+
+def _sample_rows(n, count, seed):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(n, size=min(n, count), replace=False).tolist()) | {0, n - 1}
+    return np.array(sorted(rows))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["nemotron_direct_bf16", "latent_bf16"])
+def test_full_size_sampled(ml, name):
+    wl = wlm.WORKLOADS[name]
+    r = run_layer(ml, wl, wl.N, seed=0)
+    Wn = pu.oracle_weights(r["W"], lazy_experts=True)
+    # Every token's ids (gate on all rows is cheap), then sampled outputs.
+    ref_ids, margin, _ = pu.oracle_routing(r["x"], Wn, wl)
+    pu.check_ids(r["ids"], ref_ids, margin)
+    rows = _sample_rows(wl.N, 40, 1)
+    print("errors", pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"], rows=rows))
+
+
+@pytest.mark.parametrize("n", wlm.DECODE_NS)
+def test_decode_zipf_full(ml, n):
+    wl = wlm.WORKLOADS["decode_zipf_bf16"]
+    r = run_layer(ml, wl, n, seed=0)
+    Wn = pu.oracle_weights(r["W"], lazy_experts=True)
+    print("errors", pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"]))

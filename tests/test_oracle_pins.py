@@ -138,6 +138,17 @@ def test_topk_all_equal_and_k_equals_E():
     assert np.isinf(margin).all()
 
 
+def test_rank_margin_brute_force():
+    rng = _rng(21)
+    s = (rng.integers(0, 40, size=(300, 10)) / 64.0).astype(np.float32)
+    for k in (1, 3, 9, 10):
+        m = mo.rank_margin(s, k)
+        for t in range(s.shape[0]):
+            top = sorted((float(v) for v in s[t]), reverse=True)[:k + 1]
+            gaps = [top[i] - top[i + 1] for i in range(len(top) - 1)]
+            assert m[t] == (min(gaps) if gaps else np.inf)
+
+
 # ---------------------------------------------------------------- weights --
 
 def test_routing_weights_invariants():
