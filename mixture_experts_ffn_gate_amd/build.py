@@ -34,9 +34,9 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, verbose: bool, build_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [_hipcc(), *HIP_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -49,20 +49,24 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link the shared library; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, extra_flags=(), out: str = LIB, build_dir: str = BUILD) -> str:
+    """Compile every source and link the shared library; returns its path.
+
+    ``extra_flags`` (e.g. ``-D`` tuning macros) and ``out``/``build_dir`` let a
+    caller build a variant next to the default library."""
+    os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, tuple(extra_flags)),
+                           SOURCES))
+    tmp = out + ".tmp"
     cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

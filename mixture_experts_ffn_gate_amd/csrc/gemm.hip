@@ -25,6 +25,8 @@
 //     XOR-swizzled 16-byte chunks so the MFMA operand reads are conflict-free)
 //     and shared by the 4 waves.
 //   * Weights for step k+1 are in flight while step k computes.
+#include <algorithm>
+
 #include "kernels.h"
 
 // ---------------------------------------------------------------------------
@@ -149,8 +151,23 @@ template <> struct store4<bf16> {
   }
 };
 
-template <int WF, int BMT, int EPI, typename TC>
-__global__ void __launch_bounds__(256) gemm_mfma_kernel(GemmArgs a) {
+#ifndef MOE_WEIGHT_NT
+#define MOE_WEIGHT_NT 1
+#endif
+// Weights are read exactly once per forward: non-temporal loads stream them
+// past the caches, leaving L2 to the activation rows that are reused.
+__device__ __forceinline__ bf16x8 ld_weight(const bf16* p) {
+#if MOE_WEIGHT_NT
+  return __builtin_nontemporal_load((const bf16x8*)p);
+#else
+  return *(const bf16x8*)p;
+#endif
+}
+
+template <int WF, int BMT, int EPI, typename TC, int PF>
+__global__ void __launch_bounds__(256) gemm_mfma_kernel(GemmArgs a, int nft, int slots,
+                                                        int wg_per_xcd) {
+  static_assert(PF == 1, "one weight step in flight (branch-free pipeline)");
   constexpr int FT = WF / 16;      // 16-feature tiles per wave
   constexpr int TT = BMT / 16;     // 16-row tiles per workgroup
   constexpr int BK = 64;           // k per step (two MFMA k-chunks of 32)
@@ -158,20 +175,32 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(GemmArgs a) {
   constexpr int LPASS = (CHUNKS + 255) / 256;
   __shared__ __attribute__((aligned(16))) bf16 xs[2][BMT * BK];
 
-  TileInfo ti;
-  if (!decode_tile(a, blockIdx.y, BMT, ti)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nsteps = a.K / BK;
   const int KC = a.K / 32;
+  // Persistent schedule: workgroup b runs on XCD b % 8 and walks that XCD's
+  // items (row tile x + 8*j, feature tile f), item = j * nft + f, in steps of
+  // the XCD's workgroup count. Items are row-tile major, so the workgroups of
+  // an XCD work on the feature tiles of the same row tiles (one expert's rows)
+  // at the same time and its L2 holds their activation rows.
+  const int xcd = blockIdx.x & 7;
+  const int live = a.tiles ? min(*a.num_tiles, slots) : slots;
+  const int xslots = live > xcd ? (live - xcd + 7) / 8 : 0;
+  const int items = xslots * nft;
+  for (int item = blockIdx.x >> 3; item < items; item += wg_per_xcd) {
+  const int slot = xcd + 8 * (item / nft);
+  const int ftile = item % nft;
+  TileInfo ti;
+  if (!decode_tile(a, slot, BMT, ti)) continue;
 
-  // Activation loader: chunk c = tid + 256*i -> row c/8, 16-byte chunk c%8.
+  // Activation loader: chunk c = (tid + 256*i) % CHUNKS -> row c/8, 16-byte
+  // chunk c%8 (small tiles: several threads load the same chunk, so every
+  // load is unconditional and the loop has no branches).
   const bf16* asrc[LPASS];
   int lds_off[LPASS];
-  bool lact[LPASS];
 #pragma unroll
   for (int i = 0; i < LPASS; ++i) {
-    const int c = tid + 256 * i;
-    lact[i] = c < CHUNKS;
+    const int c = (tid + 256 * i) % CHUNKS;
     const int row = c >> 3, ch = c & 7;
     const int r = min(row, ti.rows - 1);
     const int arow = a_row_of(a, ti.row0 + r);
@@ -180,7 +209,7 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(GemmArgs a) {
   }
 
   // Weight fragments of this wave: feature tile ft starts at nf0 + 16*ft.
-  const int nf0 = blockIdx.x * (4 * WF) + wave * WF;
+  const int nf0 = ftile * (4 * WF) + wave * WF;
   const bf16* W = (const bf16*)a.B + (size_t)ti.g * a.b_gstride;
   const bf16* wptr[FT];
 #pragma unroll
@@ -196,36 +225,23 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(GemmArgs a) {
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) acc[ft][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  bf16x8 wcur[FT][2], wnxt[FT][2];
+  // Two weight register sets: step ks computes from one while the loads of
+  // step ks+1 land in the other (the loop is unrolled by two so that both sets
+  // stay live and the loads are issued ahead of the MFMAs).
+  bf16x8 wA[FT][2], wB[FT][2];
   bf16x8 areg[LPASS];
-
-  // Prologue: step 0 activations -> LDS buffer 0, step 0 weights -> registers.
-#pragma unroll
-  for (int i = 0; i < LPASS; ++i)
-    if (lact[i]) areg[i] = *(const bf16x8*)(asrc[i]);
 #pragma unroll
   for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
-    for (int s = 0; s < 2; ++s) wcur[ft][s] = *(const bf16x8*)(wptr[ft] + s * 512);
+    for (int s = 0; s < 2; ++s) wA[ft][s] = ld_weight(wptr[ft] + s * 512);
 #pragma unroll
-  for (int i = 0; i < LPASS; ++i)
-    if (lact[i]) *(bf16x8*)(&xs[0][lds_off[i]]) = areg[i];
+  for (int i = 0; i < LPASS; ++i) areg[i] = *(const bf16x8*)(asrc[i]);
+#pragma unroll
+  for (int i = 0; i < LPASS; ++i) *(bf16x8*)(&xs[0][lds_off[i]]) = areg[i];
   __syncthreads();
 
   const int brow = lane & 15, bch = lane >> 4;
-  for (int ks = 0; ks < nsteps; ++ks) {
-    const int cur = ks & 1;
-    const bool more = ks + 1 < nsteps;
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < LPASS; ++i)
-        if (lact[i]) areg[i] = *(const bf16x8*)(asrc[i] + (ks + 1) * BK);
-#pragma unroll
-      for (int ft = 0; ft < FT; ++ft)
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-          wnxt[ft][s] = *(const bf16x8*)(wptr[ft] + ((size_t)(ks + 1) * 2 + s) * 512);
-    }
+  auto compute = [&](int cur, const bf16x8 (&w)[FT][2]) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       bf16x8 xf[TT];
@@ -239,19 +255,39 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(GemmArgs a) {
       for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt)
-          acc[ft][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wcur[ft][s], xf[tt], acc[ft][tt],
+          acc[ft][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[ft][s], xf[tt], acc[ft][tt],
                                                                 0, 0, 0);
     }
-    if (more) {
+  };
+  // One step with the loads of step ks+1 in flight: activations first, then
+  // weights, so that the LDS store of the activations waits only for their own
+  // loads and the weight loads stay in flight across the barrier.
+  auto step = [&](int ks, const bf16x8 (&wc)[FT][2], bf16x8 (&wn)[FT][2]) {
+    const int cur = ks & 1;
 #pragma unroll
-      for (int i = 0; i < LPASS; ++i)
-        if (lact[i]) *(bf16x8*)(&xs[cur ^ 1][lds_off[i]]) = areg[i];
+    for (int i = 0; i < LPASS; ++i) areg[i] = *(const bf16x8*)(asrc[i] + (ks + 1) * BK);
 #pragma unroll
-      for (int ft = 0; ft < FT; ++ft)
+    for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
-        for (int s = 0; s < 2; ++s) wcur[ft][s] = wnxt[ft][s];
-    }
+      for (int s = 0; s < 2; ++s)
+        wn[ft][s] = ld_weight(wptr[ft] + ((size_t)(ks + 1) * 2 + s) * 512);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
+    compute(cur, wc);
+#pragma unroll
+    for (int i = 0; i < LPASS; ++i) *(bf16x8*)(&xs[cur ^ 1][lds_off[i]]) = areg[i];
     __syncthreads();
+  };
+
+  int ks = 0;
+  for (; ks + 2 < nsteps; ks += 2) {  // branch-free steady state
+    step(ks, wA, wB);
+    step(ks + 1, wB, wA);
+  }
+  if (ks + 1 < nsteps) {  // two steps left
+    step(ks, wA, wB);
+    compute((ks + 1) & 1, wB);
+  } else {                // one step left
+    compute(ks & 1, wA);
   }
 
   // Epilogue: lane holds features nf0 + 16*ft + 4*(lane/16) + 0..3 of row 16*tt + lane%16.
@@ -277,36 +313,218 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(GemmArgs a) {
       store4<TC>::st(C + (size_t)p * a.ldc + n, v);
     }
   }
+  __syncthreads();  // LDS is reused by the next item
+  }
 }
 
-template <int WF, int BMT>
-static hipError_t launch_mfma_shape(const GemmArgs& a, int epi, bool tc_bf16, int grid_y,
-                                    hipStream_t s) {
-  dim3 grid((a.N + 4 * WF - 1) / (4 * WF), grid_y);
+// ---------------------------------------------------------------------------
+// Streaming grouped GEMM for few rows per expert (the HBM-bound regime).
+//   * No LDS and no barriers: each wave streams its own WF weight rows
+//     (pre-tiled, 1 KiB per MFMA fragment) and loads its MFMA B operands (the
+//     gathered activation rows) straight from L2, so waves never wait on each
+//     other and the weight stream keeps PF k-steps in flight per wave.
+//   * XCD-aware block order: the dispatcher deals consecutive workgroups to
+//     the 8 XCDs round-robin, so block b runs on XCD b % 8. Block b maps to
+//     row tile (b % 8) + 8 * ((b / 8) / nft) and feature tile (b / 8) % nft:
+//     every feature tile of a row tile lands on the same XCD, and that XCD's
+//     L2 fetches the tile's activation rows once.
+// ---------------------------------------------------------------------------
+template <int WF, int BMT, int EPI, typename TC, int PF>
+__global__ void __launch_bounds__(256) gemm_stream_kernel(GemmArgs a, int nft, int slots) {
+  constexpr int FT = WF / 16;
+  constexpr int TT = BMT / 16;
+  const int b = blockIdx.x;
+  const int local = b >> 3;
+  const int slot = (b & 7) + 8 * (local / nft);
+  const int ftile = local - (local / nft) * nft;
+  if (slot >= slots) return;
+  TileInfo ti;
+  if (!decode_tile(a, slot, BMT, ti)) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nf0 = ftile * (4 * WF) + wave * WF;
+  if (nf0 >= a.N) return;  // no barriers below: a wave may leave early
+  const int nsteps = a.K / 64;
+  const int KC = a.K / 32;
+
+  const bf16* xp[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+    const int r = min(tt * 16 + (lane & 15), ti.rows - 1);
+    xp[tt] = (const bf16*)a.A + (size_t)a_row_of(a, ti.row0 + r) * a.lda + (lane >> 4) * 8;
+  }
+  const bf16* W = (const bf16*)a.B + (size_t)ti.g * a.b_gstride;
+  const bf16* wp[FT];
+#pragma unroll
+  for (int ft = 0; ft < FT; ++ft) {
+    int rt = (nf0 >> 4) + ft;
+    if (rt * 16 >= a.N) rt = 0;  // dead tile: valid memory, never stored
+    wp[ft] = W + ((size_t)rt * KC * 64 + lane) * 8;
+  }
+
+  floatx4 acc[FT][TT];
+#pragma unroll
+  for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) acc[ft][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  bf16x8 wr[PF][FT][2];
+  bf16x8 xr[PF][TT][2];
+#pragma unroll
+  for (int p = 0; p < PF; ++p) {
+    if (p < nsteps) {
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+          wr[p][ft][s2] = *(const bf16x8*)(wp[ft] + ((size_t)p * 2 + s2) * 512);
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) xr[p][tt][s2] = *(const bf16x8*)(xp[tt] + p * 64 + s2 * 32);
+    }
+  }
+  for (int k0 = 0; k0 < nsteps; k0 += PF) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      const int step = k0 + p;
+      if (step < nsteps) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt)
+              acc[ft][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wr[p][ft][s2], xr[p][tt][s2],
+                                                                    acc[ft][tt], 0, 0, 0);
+        const int nxt = step + PF;
+        if (nxt < nsteps) {
+#pragma unroll
+          for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+              wr[p][ft][s2] = *(const bf16x8*)(wp[ft] + ((size_t)nxt * 2 + s2) * 512);
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+              xr[p][tt][s2] = *(const bf16x8*)(xp[tt] + nxt * 64 + s2 * 32);
+        }
+      }
+    }
+  }
+
+  TC* C = (TC*)a.C;
+#pragma unroll
+  for (int ft = 0; ft < FT; ++ft) {
+    const int n = nf0 + ft * 16 + 4 * (lane >> 4);
+    if (n >= a.N) continue;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const int r = tt * 16 + (lane & 15);
+      if (r >= ti.rows) continue;
+      const int p = ti.row0 + r;
+      floatx4 v = acc[ft][tt];
+      if (EPI == EPI_RELU2) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = relu2(v[q]);
+      }
+      if (EPI == EPI_ADD_RES) {
+        v += store4<TC>::ld((const TC*)a.res + (size_t)p * a.ldc + n);
+        if (a.add) v += *(const floatx4*)(a.add + (size_t)p * a.ldc + n);
+      }
+      store4<TC>::st(C + (size_t)p * a.ldc + n, v);
+    }
+  }
+}
+
+template <int WF, int BMT, int PF>
+static hipError_t launch_stream_shape(const GemmArgs& a, int epi, bool tc_bf16, int slots,
+                                      hipStream_t s) {
+  const int nft = (a.N + 4 * WF - 1) / (4 * WF);
+  const int blocks = 8 * nft * ((slots + 7) / 8);
+  dim3 grid(blocks);
   if (tc_bf16) {
     switch (epi) {
-      case EPI_RELU2: hipLaunchKernelGGL((gemm_mfma_kernel<WF, BMT, EPI_RELU2, bf16>), grid, dim3(256), 0, s, a); break;
-      case EPI_STORE: hipLaunchKernelGGL((gemm_mfma_kernel<WF, BMT, EPI_STORE, bf16>), grid, dim3(256), 0, s, a); break;
-      case EPI_ADD_RES: hipLaunchKernelGGL((gemm_mfma_kernel<WF, BMT, EPI_ADD_RES, bf16>), grid, dim3(256), 0, s, a); break;
+      case EPI_RELU2: hipLaunchKernelGGL((gemm_stream_kernel<WF, BMT, EPI_RELU2, bf16, PF>), grid, dim3(256), 0, s, a, nft, slots); break;
+      case EPI_STORE: hipLaunchKernelGGL((gemm_stream_kernel<WF, BMT, EPI_STORE, bf16, PF>), grid, dim3(256), 0, s, a, nft, slots); break;
+      case EPI_ADD_RES: hipLaunchKernelGGL((gemm_stream_kernel<WF, BMT, EPI_ADD_RES, bf16, PF>), grid, dim3(256), 0, s, a, nft, slots); break;
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (epi) {
-      case EPI_RELU2: hipLaunchKernelGGL((gemm_mfma_kernel<WF, BMT, EPI_RELU2, float>), grid, dim3(256), 0, s, a); break;
-      case EPI_STORE: hipLaunchKernelGGL((gemm_mfma_kernel<WF, BMT, EPI_STORE, float>), grid, dim3(256), 0, s, a); break;
+      case EPI_RELU2: hipLaunchKernelGGL((gemm_stream_kernel<WF, BMT, EPI_RELU2, float, PF>), grid, dim3(256), 0, s, a, nft, slots); break;
+      case EPI_STORE: hipLaunchKernelGGL((gemm_stream_kernel<WF, BMT, EPI_STORE, float, PF>), grid, dim3(256), 0, s, a, nft, slots); break;
       default: return hipErrorInvalidValue;
     }
   }
   return hipGetLastError();
 }
 
+hipError_t launch_gemm_stream(const GemmArgs& a, MfmaCfg cfg, int epi, bool tc_bf16, int slots,
+                              hipStream_t s) {
+  if (cfg.wf == 16 && cfg.bmt == 16) return launch_stream_shape<16, 16, 4>(a, epi, tc_bf16, slots, s);
+  if (cfg.wf == 32 && cfg.bmt == 32) return launch_stream_shape<32, 32, 3>(a, epi, tc_bf16, slots, s);
+  if (cfg.wf == 32 && cfg.bmt == 64) return launch_stream_shape<32, 64, 2>(a, epi, tc_bf16, slots, s);
+  return hipErrorInvalidValue;
+}
+
+template <int WF, int BMT, int EPI, typename TC, int PF>
+static hipError_t launch_persistent(const GemmArgs& a, int slots, hipStream_t s) {
+  static int occ = 0;  // resident workgroups per CU (queried once per process)
+  if (occ == 0) {
+    int o = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &o, (const void*)gemm_mfma_kernel<WF, BMT, EPI, TC, PF>, 256, 0) != hipSuccess || o < 1)
+      o = 1;
+    occ = o;
+  }
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n < 8)
+      n = 256;
+    cus = n;
+  }
+  const int nft = (a.N + 4 * WF - 1) / (4 * WF);
+  const int max_items_per_xcd = ((slots + 7) / 8) * nft;
+  const int wg_per_xcd = std::max(1, std::min(max_items_per_xcd, (cus / 8) * occ));
+  hipLaunchKernelGGL((gemm_mfma_kernel<WF, BMT, EPI, TC, PF>), dim3(8 * wg_per_xcd), dim3(256), 0,
+                     s, a, nft, slots, wg_per_xcd);
+  return hipGetLastError();
+}
+
+template <int WF, int BMT, int PF>
+static hipError_t launch_mfma_shape(const GemmArgs& a, int epi, bool tc_bf16, int slots,
+                                    hipStream_t s) {
+  if (tc_bf16) {
+    switch (epi) {
+      case EPI_RELU2: return launch_persistent<WF, BMT, EPI_RELU2, bf16, PF>(a, slots, s);
+      case EPI_STORE: return launch_persistent<WF, BMT, EPI_STORE, bf16, PF>(a, slots, s);
+      case EPI_ADD_RES: return launch_persistent<WF, BMT, EPI_ADD_RES, bf16, PF>(a, slots, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch (epi) {
+    case EPI_RELU2: return launch_persistent<WF, BMT, EPI_RELU2, float, PF>(a, slots, s);
+    case EPI_STORE: return launch_persistent<WF, BMT, EPI_STORE, float, PF>(a, slots, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+#ifndef MOE_MFMA_PF
+#define MOE_MFMA_PF 1
+#endif
+
 hipError_t launch_gemm_mfma(const GemmArgs& a, MfmaCfg cfg, int epi, bool tc_bf16, bool nvfp4,
-                            int grid_y, hipStream_t s) {
+                            int slots, hipStream_t s) {
   if (nvfp4) return hipErrorInvalidValue;  // NVFP4 weights use their own kernel
-  if (cfg.wf == 16 && cfg.bmt == 16) return launch_mfma_shape<16, 16>(a, epi, tc_bf16, grid_y, s);
-  if (cfg.wf == 32 && cfg.bmt == 32) return launch_mfma_shape<32, 32>(a, epi, tc_bf16, grid_y, s);
-  if (cfg.wf == 32 && cfg.bmt == 64) return launch_mfma_shape<32, 64>(a, epi, tc_bf16, grid_y, s);
-  if (cfg.wf == 32 && cfg.bmt == 128) return launch_mfma_shape<32, 128>(a, epi, tc_bf16, grid_y, s);
+  constexpr int PF = MOE_MFMA_PF;
+  if (cfg.wf == 16 && cfg.bmt == 16) return launch_mfma_shape<16, 16, PF>(a, epi, tc_bf16, slots, s);
+  if (cfg.wf == 32 && cfg.bmt == 32) return launch_mfma_shape<32, 32, PF>(a, epi, tc_bf16, slots, s);
+  if (cfg.wf == 32 && cfg.bmt == 64) return launch_mfma_shape<32, 64, PF>(a, epi, tc_bf16, slots, s);
+  if (cfg.wf == 32 && cfg.bmt == 128) return launch_mfma_shape<32, 128, PF>(a, epi, tc_bf16, slots, s);
   return hipErrorInvalidValue;
 }
 

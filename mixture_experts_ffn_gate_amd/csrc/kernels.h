@@ -60,6 +60,11 @@ struct MfmaCfg {
 hipError_t launch_gemm_mfma(const GemmArgs& a, MfmaCfg cfg, int epi, bool tc_bf16, bool nvfp4,
                             int grid_y, hipStream_t s);
 
+// Barrier-free streaming grouped/dense GEMM for few rows per tile (wf, bmt in
+// {16,16}, {32,32}, {32,64}); `slots` row tiles (grouped: tile-list capacity).
+hipError_t launch_gemm_stream(const GemmArgs& a, MfmaCfg cfg, int epi, bool tc_bf16, int slots,
+                              hipStream_t s);
+
 // Re-tile bf16 [G][N][K] row-major weights into the MFMA lane order.
 hipError_t launch_retile_bf16(const bf16* src, bf16* dst, int G, int N, int K, hipStream_t s);
 

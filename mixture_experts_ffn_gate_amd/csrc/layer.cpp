@@ -31,6 +31,10 @@
 
 #include "kernels.h"
 
+#ifndef MOE_USE_STREAM_GEMM
+#define MOE_USE_STREAM_GEMM 0
+#endif
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -201,10 +205,13 @@ MfmaCfg grouped_cfg(int rows_per_group) {
   return {32, 128};
 }
 
+#ifndef MOE_DENSE_BMT
+#define MOE_DENSE_BMT 64
+#endif
 MfmaCfg dense_cfg(int n) {
   if (n <= 16) return {16, 16};
   if (n <= 32) return {32, 32};
-  if (n <= 64) return {32, 64};
+  if (n <= 64 || MOE_DENSE_BMT == 64) return {32, 64};
   return {32, 128};
 }
 
@@ -212,7 +219,12 @@ int gemm(moe_layer* L, const GemmArgs& a, int epi, bool out_bf16, int bm_or_cfg_
          MfmaCfg cfg, int grid_y, hipStream_t s, const char* what) {
   hipError_t e;
   if (L->mfma) {
-    e = launch_gemm_mfma(a, cfg, epi, out_bf16, false, grid_y, s);
+#if MOE_USE_STREAM_GEMM
+    if (cfg.bmt <= 64)
+      e = launch_gemm_stream(a, cfg, epi, out_bf16, grid_y, s);
+    else
+#endif
+      e = launch_gemm_mfma(a, cfg, epi, out_bf16, false, grid_y, s);
   } else {
     (void)bm_or_cfg_rows;
     e = launch_gemm_simt_f32(a, epi, grid_y, s);

@@ -100,6 +100,115 @@ __global__ void __launch_bounds__(256) norm_gate_kernel(const TA* __restrict__ h
 }
 
 // ---------------------------------------------------------------------------
+// Fused RMSNorm + gate for bf16 layers, on MFMA.
+// Block = 4 waves, 16 tokens x experts [blockIdx.y * epb, +epb) (epb % 16 == 0).
+//   1. inverse RMS of the 16 rows (each wave 4 rows)
+//   2. the 32-wide k-steps of the hidden dimension are dealt round-robin to the
+//      waves; a lane builds the MFMA B operand (token lane%16, k-elements
+//      8*(lane/16)..+7) from hidden * rinv * gamma in fp32, writes normed
+//      (bf16) and residual once (blockIdx.y == 0), and splits the fp32 value
+//      into hi = bf16(n) and lo = bf16(n - hi). Two MFMAs per expert tile,
+//      W_g x hi + W_g x lo, give logits with ~16 mantissa bits of n: the top-k
+//      decision sees (nearly) the fp32 normed vector, not its bf16 rounding.
+//   3. the four waves' partial sums meet in LDS and are added in wave order.
+// Output lane layout: experts 4*(lane/16)+0..3 of token lane%16 (16-byte store).
+// ---------------------------------------------------------------------------
+template <int ET>  // expert tiles of 16 per block
+__global__ void __launch_bounds__(256) norm_gate_mfma_kernel(const bf16* __restrict__ hidden,
+                                                             const bf16* __restrict__ gamma,
+                                                             const bf16* __restrict__ wgate,
+                                                             bf16* __restrict__ normed,
+                                                             bf16* __restrict__ residual,
+                                                             float* __restrict__ logits, int n,
+                                                             int H, int E, float eps) {
+  __shared__ float rinv[16];
+  __shared__ floatx4 red[4][ET][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * 16;
+  const int e0 = blockIdx.y * ET * 16;
+
+  // 1. inverse RMS (each wave: rows wave*4 .. +3; 16-byte loads)
+  for (int t = wave * 4; t < wave * 4 + 4; ++t) {
+    float ss = 0.f;
+    if (t0 + t < n) {
+      const bf16* x = hidden + (size_t)(t0 + t) * H;
+      for (int i = lane * 8; i < H; i += 512) {
+        const bf16x8 v = *(const bf16x8*)(x + i);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float f = (float)v[q];
+          ss += f * f;
+        }
+      }
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) rinv[t] = 1.0f / sqrtf(ss / (float)H + eps);
+  }
+  __syncthreads();
+
+  // 2. k-steps of 32, dealt round-robin to the waves
+  const int tok = lane & 15, kg = lane >> 4;
+  const bool tvalid = t0 + tok < n;
+  const float rv = rinv[tok];
+  const bool writer = blockIdx.y == 0;
+  const bf16* wbase[ET];
+#pragma unroll
+  for (int et = 0; et < ET; ++et) {
+    const int e = min(e0 + et * 16 + tok, E - 1);  // rows past E: valid memory, never stored
+    wbase[et] = wgate + (size_t)e * H + kg * 8;
+  }
+  floatx4 acc[ET];
+#pragma unroll
+  for (int et = 0; et < ET; ++et) acc[et] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const size_t row = (size_t)(t0 + tok) * H + kg * 8;
+  for (int k0 = wave * 32; k0 < H; k0 += 128) {
+    bf16x8 wf[ET];
+#pragma unroll
+    for (int et = 0; et < ET; ++et) wf[et] = *(const bf16x8*)(wbase[et] + k0);
+    bf16x8 xv = {};
+    if (tvalid) xv = *(const bf16x8*)(hidden + row + k0);
+    const bf16x8 gv = *(const bf16x8*)(gamma + k0 + kg * 8);
+    bf16x8 hi, lo, nb;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float v = (float)xv[q] * rv * (float)gv[q];
+      hi[q] = (bf16)v;
+      lo[q] = (bf16)(v - (float)hi[q]);
+      nb[q] = hi[q];
+    }
+    if (writer && tvalid) {
+      *(bf16x8*)(residual + row + k0) = xv;
+      *(bf16x8*)(normed + row + k0) = nb;
+    }
+#pragma unroll
+    for (int et = 0; et < ET; ++et) {
+      acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[et], hi, acc[et], 0, 0, 0);
+      acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[et], lo, acc[et], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int et = 0; et < ET; ++et) red[wave][et][lane] = acc[et];
+  __syncthreads();
+
+  // 3. cross-wave sum (wave w finishes tiles w, w+4, ...), fixed order
+  for (int et = wave; et < ET; et += 4) {
+    floatx4 v = red[0][et][lane];
+    v += red[1][et][lane];
+    v += red[2][et][lane];
+    v += red[3][et][lane];
+    const int e = e0 + et * 16 + 4 * kg;
+    if (tvalid && e < E) {
+      float* dst = logits + (size_t)(t0 + tok) * E + e;
+      if (e + 3 < E && (E & 3) == 0) {
+        *(floatx4*)dst = v;
+      } else {
+        for (int q = 0; q < 4 && e + q < E; ++q) dst[q] = v[q];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Sigmoid top-k. One wave64 per token; lane l holds experts l, l+64, ...
 // Selection key = (fp32 bits of the score) << 32 | (0xFFFFFFFF - e): scores
 // lie in [0, 1], so their bit patterns order like the values, and among equal
@@ -279,7 +388,28 @@ static void norm_gate_tm(int act_dt, const void* hidden, const void* gamma, cons
 hipError_t launch_norm_gate(int act_dt, const void* hidden, const void* gamma, const void* wgate,
                             void* normed, void* residual, float* logits, int n, int H, int E,
                             float eps, hipStream_t s) {
-  // TM fp32 rows of H stay in LDS; keep them within 60 KiB.
+  if (act_dt == MOE_DT_BF16) {
+    // 16 tokens per block; split the expert tiles over blockIdx.y until the
+    // grid has >= 512 blocks (at least one 16-expert tile per block).
+    const int bx = (n + 15) / 16;
+    const int tiles = (E + 15) / 16;
+    int et = tiles;
+    while (et > 1 && bx * ((tiles + et - 1) / et) < 512) et = (et + 1) / 2;
+    et = et >= 8 ? 8 : et >= 4 ? 4 : et >= 2 ? 2 : 1;
+    dim3 grid(bx, (tiles + et - 1) / et);
+    switch (et) {
+#define NG_CASE(X)                                                                           \
+  case X:                                                                                    \
+    hipLaunchKernelGGL((norm_gate_mfma_kernel<X>), grid, dim3(256), 0, s, (const bf16*)hidden, \
+                       (const bf16*)gamma, (const bf16*)wgate, (bf16*)normed, (bf16*)residual, \
+                       logits, n, H, E, eps);                                                \
+    break;
+      NG_CASE(1) NG_CASE(2) NG_CASE(4) NG_CASE(8)
+#undef NG_CASE
+    }
+    return hipGetLastError();
+  }
+  // fp32 layers: SIMT kernel; TM fp32 rows of H stay in LDS (<= 60 KiB).
   if (H * 4 * 4 <= 60 * 1024)
     norm_gate_tm<4>(act_dt, hidden, gamma, wgate, normed, residual, logits, n, H, E, eps, s);
   else if (H * 2 * 4 <= 60 * 1024)

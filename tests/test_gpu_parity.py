@@ -187,6 +187,26 @@ def test_sort_stage_bit_exact_inside_forward(ml):
         np.testing.assert_array_equal(bufs[nm].cpu().numpy(), ref, err_msg=nm)
 
 
+@pytest.mark.parametrize("name", ["direct_ragged", "latent_ragged"])
+def test_gate_logits_and_normed_inside_forward(ml, name):
+    # The gate is fed the fp32 normed vector (split into bf16 hi + lo parts):
+    # logits agree with the float64 oracle far below the top-k margin bar.
+    wl = SMALL[name]
+    r = run_layer(ml, wl, wl.N, seed=9)
+    logits = torch.empty(wl.N, wl.E, dtype=torch.float32, device="cuda")
+    normed = torch.empty(wl.N, wl.H, dtype=torch.bfloat16, device="cuda")
+    r["layer"].debug_read("logits", logits)
+    r["layer"].debug_read("normed", normed)
+    torch.cuda.synchronize()
+    Wn = pu.oracle_weights(r["W"])
+    n64 = mo.rms_norm(r["x"], Wn["gamma"], wl.eps)
+    ref = mo.gate_logits(n64, Wn["gate"])
+    assert np.max(np.abs(logits.cpu().numpy() - ref)) < 2e-4
+    # normed is the bf16 rounding of the fp32 value: within one bf16 ulp.
+    nb = f32np(normed)
+    assert np.all(np.abs(nb - n64) <= 2.0 ** -8 * np.abs(n64) + 1e-30)
+
+
 def test_residual_input_ignored_and_deterministic(ml):
     wl = SMALL["direct_ragged"]
     W = wlm.make_weights(wl, 4, "cuda")
