@@ -25,6 +25,10 @@
 //     XOR-swizzled 16-byte chunks so the MFMA operand reads are conflict-free)
 //     and shared by the 4 waves.
 //   * Weights for step k+1 are in flight while step k computes.
+//   * NVFP4 weights (4-bit E2M1 + E4M3 per 16 along K + fp32 scale2 per
+//     matrix; page "metrale_model_arch/nemotron_moe.rs", `ExpertPtrTable`) are
+//     re-tiled the same way and dequantized in registers to exact bf16 before
+//     the MFMA; scale2 multiplies the accumulator in the epilogue.
 #include <algorithm>
 
 #include "kernels.h"
@@ -156,325 +160,252 @@ template <> struct store4<bf16> {
 #endif
 // Weights are read exactly once per forward: non-temporal loads stream them
 // past the caches, leaving L2 to the activation rows that are reused.
-__device__ __forceinline__ bf16x8 ld_weight(const bf16* p) {
+template <typename T>
+__device__ __forceinline__ T ld_stream(const T* p) {
 #if MOE_WEIGHT_NT
-  return __builtin_nontemporal_load((const bf16x8*)p);
+  return __builtin_nontemporal_load(p);
 #else
-  return *(const bf16x8*)p;
+  return *p;
 #endif
 }
 
-template <int WF, int BMT, int EPI, typename TC, int PF>
+// E4M3 (bias 7, no infinities) scale byte -> fp32 (exact).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+}
+
+// Eight E2M1 codes (nibble i = element i) times an fp32 block scale -> bf16.
+// e2m1 * e4m3 has at most 6 significant bits, so every product is exact in bf16.
+__device__ __forceinline__ bf16x8 dequant8(uint32_t q, float sc) {
+  bf16x8 o;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t c = (q >> (4 * i)) & 15u, mag = c & 7u;
+    // magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6: for mag >= 2 the fp32 bits are
+    // (mag << 22) + (126 << 23); mag 1 is 0.5 and mag 0 is 0.
+    uint32_t bits = mag >= 2u ? (mag << 22) + (126u << 23) : (mag ? (126u << 23) : 0u);
+    bits |= (c & 8u) << 28;
+    o[i] = (bf16)(__uint_as_float(bits) * sc);
+  }
+  return o;
+}
+
+// Weight fragment sources of the MFMA kernel. A fragment is what one wave
+// consumes per 64-wide k-step for its FT 16-row tiles.
+//  * bf16: pre-tiled [N/16][K/32][64 lanes][8]: lane l holds row l%16, k
+//    8*(l/16)..+7 of a 16x32 block (1 KiB per block, one contiguous read).
+//  * NVFP4: pre-tiled packed nibbles [N/16][K/64][64 lanes][8 bytes] (dword s
+//    holds the lane's 8 codes of k-chunk s) and block scales
+//    [N/16][K/64][16 rows][4 bytes] (the row's four 16-element blocks of the
+//    step); scale2 of the group multiplies the accumulator in the epilogue.
+template <int WQ, int FT> struct WSrc;
+
+template <int FT> struct WSrc<0, FT> {
+  struct Frag { bf16x8 v[FT][2]; };
+  const bf16* p[FT];
+  __device__ __forceinline__ void init(const GemmArgs& a, int g, int nf0, int lane) {
+    const bf16* W = (const bf16*)a.B + (size_t)g * a.b_gstride;
+    const int KC = a.K / 32;
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) {
+      int rt = (nf0 >> 4) + ft;
+      if (rt * 16 >= a.N) rt = 0;  // dead tile: read valid memory, never stored
+      p[ft] = W + ((size_t)rt * KC * 64 + lane) * 8;
+    }
+  }
+  __device__ __forceinline__ void load(Frag& f, int ks) const {
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) f.v[ft][s] = ld_stream((const bf16x8*)(p[ft] + ((size_t)ks * 2 + s) * 512));
+  }
+  __device__ __forceinline__ bf16x8 get(const Frag& f, int ft, int s, int) const { return f.v[ft][s]; }
+};
+
+template <int FT> struct WSrc<1, FT> {
+  struct Frag { u32x2 q[FT]; uint32_t sc[FT]; };
+  const u32x2* pq[FT];
+  const uint32_t* ps[FT];
+  __device__ __forceinline__ void init(const GemmArgs& a, int g, int nf0, int lane) {
+    const uint8_t* Q = (const uint8_t*)a.B + (size_t)g * a.b_gstride;
+    const uint8_t* S = a.b_scales + (size_t)g * a.bs_gstride;
+    const int KS = a.K / 64;
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) {
+      int rt = (nf0 >> 4) + ft;
+      if (rt * 16 >= a.N) rt = 0;
+      pq[ft] = (const u32x2*)Q + (size_t)rt * KS * 64 + lane;
+      ps[ft] = (const uint32_t*)S + (size_t)rt * KS * 16 + (lane & 15);
+    }
+  }
+  __device__ __forceinline__ void load(Frag& f, int ks) const {
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) {
+      f.q[ft] = ld_stream(pq[ft] + (size_t)ks * 64);
+      f.sc[ft] = ps[ft][(size_t)ks * 16];
+    }
+  }
+  __device__ __forceinline__ bf16x8 get(const Frag& f, int ft, int s, int lane) const {
+    // k-chunk s of lane group g = lane/16 lies in block 2s + g/2 of the step.
+    const uint32_t sb = (f.sc[ft] >> (8 * (2 * s + (lane >> 5)))) & 0xFFu;
+    return dequant8(f.q[ft][s], e4m3_to_f32(sb));
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Persistent MFMA GEMM (grouped or dense), WQ = 0 bf16 weights, 1 NVFP4.
+// ---------------------------------------------------------------------------
+template <int WF, int BMT, int EPI, typename TC, int WQ>
 __global__ void __launch_bounds__(256) gemm_mfma_kernel(GemmArgs a, int nft, int slots,
                                                         int wg_per_xcd) {
-  static_assert(PF == 1, "one weight step in flight (branch-free pipeline)");
   constexpr int FT = WF / 16;      // 16-feature tiles per wave
   constexpr int TT = BMT / 16;     // 16-row tiles per workgroup
   constexpr int BK = 64;           // k per step (two MFMA k-chunks of 32)
   constexpr int CHUNKS = BMT * 8;  // 16-byte chunks of one activation slice
   constexpr int LPASS = (CHUNKS + 255) / 256;
+  using Src = WSrc<WQ, FT>;
+  using Frag = typename Src::Frag;
   __shared__ __attribute__((aligned(16))) bf16 xs[2][BMT * BK];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nsteps = a.K / BK;
-  const int KC = a.K / 32;
-  // Persistent schedule: workgroup b runs on XCD b % 8 and walks that XCD's
-  // items (row tile x + 8*j, feature tile f), item = j * nft + f, in steps of
+  // Persistent schedule: workgroup b runs on XCD b % 8 (the dispatcher deals
+  // consecutive workgroups to the 8 XCDs round-robin) and walks that XCD's
+  // items (row tile xcd + 8*j, feature tile f), item = j * nft + f, in steps of
   // the XCD's workgroup count. Items are row-tile major, so the workgroups of
   // an XCD work on the feature tiles of the same row tiles (one expert's rows)
-  // at the same time and its L2 holds their activation rows.
+  // at the same time and the XCD's L2 fetches those activation rows once.
   const int xcd = blockIdx.x & 7;
   const int live = a.tiles ? min(*a.num_tiles, slots) : slots;
   const int xslots = live > xcd ? (live - xcd + 7) / 8 : 0;
   const int items = xslots * nft;
   for (int item = blockIdx.x >> 3; item < items; item += wg_per_xcd) {
-  const int slot = xcd + 8 * (item / nft);
-  const int ftile = item % nft;
-  TileInfo ti;
-  if (!decode_tile(a, slot, BMT, ti)) continue;
+    const int slot = xcd + 8 * (item / nft);
+    const int ftile = item % nft;
+    TileInfo ti;
+    if (!decode_tile(a, slot, BMT, ti)) continue;
 
-  // Activation loader: chunk c = (tid + 256*i) % CHUNKS -> row c/8, 16-byte
-  // chunk c%8 (small tiles: several threads load the same chunk, so every
-  // load is unconditional and the loop has no branches).
-  const bf16* asrc[LPASS];
-  int lds_off[LPASS];
+    // Activation loader: chunk c = (tid + 256*i) % CHUNKS -> row c/8, 16-byte
+    // chunk c%8 (small tiles: several threads load the same chunk, so every
+    // load is unconditional and the k-loop has no branches).
+    const bf16* asrc[LPASS];
+    int lds_off[LPASS];
 #pragma unroll
-  for (int i = 0; i < LPASS; ++i) {
-    const int c = (tid + 256 * i) % CHUNKS;
-    const int row = c >> 3, ch = c & 7;
-    const int r = min(row, ti.rows - 1);
-    const int arow = a_row_of(a, ti.row0 + r);
-    asrc[i] = (const bf16*)a.A + (size_t)arow * a.lda + ch * 8;
-    lds_off[i] = row * BK + ((ch ^ (row & 7)) << 3);
-  }
-
-  // Weight fragments of this wave: feature tile ft starts at nf0 + 16*ft.
-  const int nf0 = ftile * (4 * WF) + wave * WF;
-  const bf16* W = (const bf16*)a.B + (size_t)ti.g * a.b_gstride;
-  const bf16* wptr[FT];
-#pragma unroll
-  for (int ft = 0; ft < FT; ++ft) {
-    int rt = (nf0 >> 4) + ft;
-    if (rt * 16 >= a.N) rt = 0;  // dead tile: read valid memory, never stored
-    wptr[ft] = W + ((size_t)rt * KC * 64 + lane) * 8;
-  }
-
-  floatx4 acc[FT][TT];
-#pragma unroll
-  for (int ft = 0; ft < FT; ++ft)
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) acc[ft][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  // Two weight register sets: step ks computes from one while the loads of
-  // step ks+1 land in the other (the loop is unrolled by two so that both sets
-  // stay live and the loads are issued ahead of the MFMAs).
-  bf16x8 wA[FT][2], wB[FT][2];
-  bf16x8 areg[LPASS];
-#pragma unroll
-  for (int ft = 0; ft < FT; ++ft)
-#pragma unroll
-    for (int s = 0; s < 2; ++s) wA[ft][s] = ld_weight(wptr[ft] + s * 512);
-#pragma unroll
-  for (int i = 0; i < LPASS; ++i) areg[i] = *(const bf16x8*)(asrc[i]);
-#pragma unroll
-  for (int i = 0; i < LPASS; ++i) *(bf16x8*)(&xs[0][lds_off[i]]) = areg[i];
-  __syncthreads();
-
-  const int brow = lane & 15, bch = lane >> 4;
-  auto compute = [&](int cur, const bf16x8 (&w)[FT][2]) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      bf16x8 xf[TT];
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) {
-        const int row = tt * 16 + brow;
-        const int ch = s * 4 + bch;
-        xf[tt] = *(const bf16x8*)(&xs[cur][row * BK + ((ch ^ (row & 7)) << 3)]);
-      }
-#pragma unroll
-      for (int ft = 0; ft < FT; ++ft)
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
-          acc[ft][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[ft][s], xf[tt], acc[ft][tt],
-                                                                0, 0, 0);
+    for (int i = 0; i < LPASS; ++i) {
+      const int c = (tid + 256 * i) % CHUNKS;
+      const int row = c >> 3, ch = c & 7;
+      const int r = min(row, ti.rows - 1);
+      const int arow = a_row_of(a, ti.row0 + r);
+      asrc[i] = (const bf16*)a.A + (size_t)arow * a.lda + ch * 8;
+      lds_off[i] = row * BK + ((ch ^ (row & 7)) << 3);
     }
-  };
-  // One step with the loads of step ks+1 in flight: activations first, then
-  // weights, so that the LDS store of the activations waits only for their own
-  // loads and the weight loads stay in flight across the barrier.
-  auto step = [&](int ks, const bf16x8 (&wc)[FT][2], bf16x8 (&wn)[FT][2]) {
-    const int cur = ks & 1;
-#pragma unroll
-    for (int i = 0; i < LPASS; ++i) areg[i] = *(const bf16x8*)(asrc[i] + (ks + 1) * BK);
+
+    const int nf0 = ftile * (4 * WF) + wave * WF;  // first feature of this wave
+    Src src;
+    src.init(a, ti.g, nf0, lane);
+
+    floatx4 acc[FT][TT];
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
-        wn[ft][s] = ld_weight(wptr[ft] + ((size_t)(ks + 1) * 2 + s) * 512);
-    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
-    compute(cur, wc);
+      for (int tt = 0; tt < TT; ++tt) acc[ft][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // Two fragment sets: step ks computes from one while the loads of step
+    // ks+1 land in the other (unrolled by two so both stay live and the loads
+    // issue ahead of the MFMAs).
+    Frag fA, fB;
+    bf16x8 areg[LPASS];
+    src.load(fA, 0);
 #pragma unroll
-    for (int i = 0; i < LPASS; ++i) *(bf16x8*)(&xs[cur ^ 1][lds_off[i]]) = areg[i];
+    for (int i = 0; i < LPASS; ++i) areg[i] = *(const bf16x8*)(asrc[i]);
+#pragma unroll
+    for (int i = 0; i < LPASS; ++i) *(bf16x8*)(&xs[0][lds_off[i]]) = areg[i];
     __syncthreads();
-  };
 
-  int ks = 0;
-  for (; ks + 2 < nsteps; ks += 2) {  // branch-free steady state
-    step(ks, wA, wB);
-    step(ks + 1, wB, wA);
-  }
-  if (ks + 1 < nsteps) {  // two steps left
-    step(ks, wA, wB);
-    compute((ks + 1) & 1, wB);
-  } else {                // one step left
-    compute(ks & 1, wA);
-  }
-
-  // Epilogue: lane holds features nf0 + 16*ft + 4*(lane/16) + 0..3 of row 16*tt + lane%16.
-  TC* C = (TC*)a.C;
+    const int brow = lane & 15, bch = lane >> 4;
+    auto compute = [&](int cur, const Frag& w) {
 #pragma unroll
-  for (int ft = 0; ft < FT; ++ft) {
-    const int n = nf0 + ft * 16 + 4 * (lane >> 4);
-    if (n >= a.N) continue;
+      for (int s = 0; s < 2; ++s) {
+        bf16x8 xf[TT];
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      const int r = tt * 16 + (lane & 15);
-      if (r >= ti.rows) continue;
-      const int p = ti.row0 + r;
-      floatx4 v = acc[ft][tt];
-      if (EPI == EPI_RELU2) {
+        for (int tt = 0; tt < TT; ++tt) {
+          const int row = tt * 16 + brow;
+          const int ch = s * 4 + bch;
+          xf[tt] = *(const bf16x8*)(&xs[cur][row * BK + ((ch ^ (row & 7)) << 3)]);
+        }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = relu2(v[q]);
-      }
-      if (EPI == EPI_ADD_RES) {
-        v += store4<TC>::ld((const TC*)a.res + (size_t)p * a.ldc + n);
-        if (a.add) v += *(const floatx4*)(a.add + (size_t)p * a.ldc + n);
-      }
-      store4<TC>::st(C + (size_t)p * a.ldc + n, v);
-    }
-  }
-  __syncthreads();  // LDS is reused by the next item
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Streaming grouped GEMM for few rows per expert (the HBM-bound regime).
-//   * No LDS and no barriers: each wave streams its own WF weight rows
-//     (pre-tiled, 1 KiB per MFMA fragment) and loads its MFMA B operands (the
-//     gathered activation rows) straight from L2, so waves never wait on each
-//     other and the weight stream keeps PF k-steps in flight per wave.
-//   * XCD-aware block order: the dispatcher deals consecutive workgroups to
-//     the 8 XCDs round-robin, so block b runs on XCD b % 8. Block b maps to
-//     row tile (b % 8) + 8 * ((b / 8) / nft) and feature tile (b / 8) % nft:
-//     every feature tile of a row tile lands on the same XCD, and that XCD's
-//     L2 fetches the tile's activation rows once.
-// ---------------------------------------------------------------------------
-template <int WF, int BMT, int EPI, typename TC, int PF>
-__global__ void __launch_bounds__(256) gemm_stream_kernel(GemmArgs a, int nft, int slots) {
-  constexpr int FT = WF / 16;
-  constexpr int TT = BMT / 16;
-  const int b = blockIdx.x;
-  const int local = b >> 3;
-  const int slot = (b & 7) + 8 * (local / nft);
-  const int ftile = local - (local / nft) * nft;
-  if (slot >= slots) return;
-  TileInfo ti;
-  if (!decode_tile(a, slot, BMT, ti)) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nf0 = ftile * (4 * WF) + wave * WF;
-  if (nf0 >= a.N) return;  // no barriers below: a wave may leave early
-  const int nsteps = a.K / 64;
-  const int KC = a.K / 32;
-
-  const bf16* xp[TT];
-#pragma unroll
-  for (int tt = 0; tt < TT; ++tt) {
-    const int r = min(tt * 16 + (lane & 15), ti.rows - 1);
-    xp[tt] = (const bf16*)a.A + (size_t)a_row_of(a, ti.row0 + r) * a.lda + (lane >> 4) * 8;
-  }
-  const bf16* W = (const bf16*)a.B + (size_t)ti.g * a.b_gstride;
-  const bf16* wp[FT];
-#pragma unroll
-  for (int ft = 0; ft < FT; ++ft) {
-    int rt = (nf0 >> 4) + ft;
-    if (rt * 16 >= a.N) rt = 0;  // dead tile: valid memory, never stored
-    wp[ft] = W + ((size_t)rt * KC * 64 + lane) * 8;
-  }
-
-  floatx4 acc[FT][TT];
-#pragma unroll
-  for (int ft = 0; ft < FT; ++ft)
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) acc[ft][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  bf16x8 wr[PF][FT][2];
-  bf16x8 xr[PF][TT][2];
-#pragma unroll
-  for (int p = 0; p < PF; ++p) {
-    if (p < nsteps) {
-#pragma unroll
-      for (int ft = 0; ft < FT; ++ft)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-          wr[p][ft][s2] = *(const bf16x8*)(wp[ft] + ((size_t)p * 2 + s2) * 512);
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) xr[p][tt][s2] = *(const bf16x8*)(xp[tt] + p * 64 + s2 * 32);
-    }
-  }
-  for (int k0 = 0; k0 < nsteps; k0 += PF) {
-#pragma unroll
-    for (int p = 0; p < PF; ++p) {
-      const int step = k0 + p;
-      if (step < nsteps) {
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-          for (int ft = 0; ft < FT; ++ft)
-#pragma unroll
-            for (int tt = 0; tt < TT; ++tt)
-              acc[ft][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wr[p][ft][s2], xr[p][tt][s2],
-                                                                    acc[ft][tt], 0, 0, 0);
-        const int nxt = step + PF;
-        if (nxt < nsteps) {
-#pragma unroll
-          for (int ft = 0; ft < FT; ++ft)
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)
-              wr[p][ft][s2] = *(const bf16x8*)(wp[ft] + ((size_t)nxt * 2 + s2) * 512);
+        for (int ft = 0; ft < FT; ++ft) {
+          const bf16x8 wf = src.get(w, ft, s, lane);
 #pragma unroll
           for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)
-              xr[p][tt][s2] = *(const bf16x8*)(xp[tt] + nxt * 64 + s2 * 32);
+            acc[ft][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf[tt], acc[ft][tt], 0, 0, 0);
         }
       }
-    }
-  }
+    };
+    // One step with the loads of step ks+1 in flight: activations first, then
+    // weights, so the LDS store of the activations waits only for their own
+    // loads and the weight loads stay in flight across the barrier.
+    auto step = [&](int ks, const Frag& wc, Frag& wn) {
+      const int cur = ks & 1;
+#pragma unroll
+      for (int i = 0; i < LPASS; ++i) areg[i] = *(const bf16x8*)(asrc[i] + (ks + 1) * BK);
+      src.load(wn, ks + 1);
+      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
+      compute(cur, wc);
+#pragma unroll
+      for (int i = 0; i < LPASS; ++i) *(bf16x8*)(&xs[cur ^ 1][lds_off[i]]) = areg[i];
+      __syncthreads();
+    };
 
-  TC* C = (TC*)a.C;
+    int ks = 0;
+    for (; ks + 2 < nsteps; ks += 2) {  // branch-free steady state
+      step(ks, fA, fB);
+      step(ks + 1, fB, fA);
+    }
+    if (ks + 1 < nsteps) {  // two steps left
+      step(ks, fA, fB);
+      compute((ks + 1) & 1, fB);
+    } else {                // one step left
+      compute(ks & 1, fA);
+    }
+
+    // Epilogue: lane holds features nf0 + 16*ft + 4*(lane/16) + 0..3 of row 16*tt + lane%16.
+    const float s2 = WQ == 1 ? a.b_scale2[ti.g] : 1.0f;
+    TC* C = (TC*)a.C;
 #pragma unroll
-  for (int ft = 0; ft < FT; ++ft) {
-    const int n = nf0 + ft * 16 + 4 * (lane >> 4);
-    if (n >= a.N) continue;
+    for (int ft = 0; ft < FT; ++ft) {
+      const int n = nf0 + ft * 16 + 4 * (lane >> 4);
+      if (n >= a.N) continue;
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      const int r = tt * 16 + (lane & 15);
-      if (r >= ti.rows) continue;
-      const int p = ti.row0 + r;
-      floatx4 v = acc[ft][tt];
-      if (EPI == EPI_RELU2) {
+      for (int tt = 0; tt < TT; ++tt) {
+        const int r = tt * 16 + (lane & 15);
+        if (r >= ti.rows) continue;
+        const int p = ti.row0 + r;
+        floatx4 v = acc[ft][tt];
+        if (WQ == 1) v *= s2;
+        if (EPI == EPI_RELU2) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = relu2(v[q]);
+          for (int q = 0; q < 4; ++q) v[q] = relu2(v[q]);
+        }
+        if (EPI == EPI_ADD_RES) {
+          v += store4<TC>::ld((const TC*)a.res + (size_t)p * a.ldc + n);
+          if (a.add) v += *(const floatx4*)(a.add + (size_t)p * a.ldc + n);
+        }
+        store4<TC>::st(C + (size_t)p * a.ldc + n, v);
       }
-      if (EPI == EPI_ADD_RES) {
-        v += store4<TC>::ld((const TC*)a.res + (size_t)p * a.ldc + n);
-        if (a.add) v += *(const floatx4*)(a.add + (size_t)p * a.ldc + n);
-      }
-      store4<TC>::st(C + (size_t)p * a.ldc + n, v);
     }
+    __syncthreads();  // LDS is reused by the next item
   }
 }
 
-template <int WF, int BMT, int PF>
-static hipError_t launch_stream_shape(const GemmArgs& a, int epi, bool tc_bf16, int slots,
-                                      hipStream_t s) {
-  const int nft = (a.N + 4 * WF - 1) / (4 * WF);
-  const int blocks = 8 * nft * ((slots + 7) / 8);
-  dim3 grid(blocks);
-  if (tc_bf16) {
-    switch (epi) {
-      case EPI_RELU2: hipLaunchKernelGGL((gemm_stream_kernel<WF, BMT, EPI_RELU2, bf16, PF>), grid, dim3(256), 0, s, a, nft, slots); break;
-      case EPI_STORE: hipLaunchKernelGGL((gemm_stream_kernel<WF, BMT, EPI_STORE, bf16, PF>), grid, dim3(256), 0, s, a, nft, slots); break;
-      case EPI_ADD_RES: hipLaunchKernelGGL((gemm_stream_kernel<WF, BMT, EPI_ADD_RES, bf16, PF>), grid, dim3(256), 0, s, a, nft, slots); break;
-      default: return hipErrorInvalidValue;
-    }
-  } else {
-    switch (epi) {
-      case EPI_RELU2: hipLaunchKernelGGL((gemm_stream_kernel<WF, BMT, EPI_RELU2, float, PF>), grid, dim3(256), 0, s, a, nft, slots); break;
-      case EPI_STORE: hipLaunchKernelGGL((gemm_stream_kernel<WF, BMT, EPI_STORE, float, PF>), grid, dim3(256), 0, s, a, nft, slots); break;
-      default: return hipErrorInvalidValue;
-    }
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_gemm_stream(const GemmArgs& a, MfmaCfg cfg, int epi, bool tc_bf16, int slots,
-                              hipStream_t s) {
-  if (cfg.wf == 16 && cfg.bmt == 16) return launch_stream_shape<16, 16, 4>(a, epi, tc_bf16, slots, s);
-  if (cfg.wf == 32 && cfg.bmt == 32) return launch_stream_shape<32, 32, 3>(a, epi, tc_bf16, slots, s);
-  if (cfg.wf == 32 && cfg.bmt == 64) return launch_stream_shape<32, 64, 2>(a, epi, tc_bf16, slots, s);
-  return hipErrorInvalidValue;
-}
-
-template <int WF, int BMT, int EPI, typename TC, int PF>
+template <int WF, int BMT, int EPI, typename TC, int WQ>
 static hipError_t launch_persistent(const GemmArgs& a, int slots, hipStream_t s) {
   static int occ = 0;  // resident workgroups per CU (queried once per process)
   if (occ == 0) {
     int o = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &o, (const void*)gemm_mfma_kernel<WF, BMT, EPI, TC, PF>, 256, 0) != hipSuccess || o < 1)
+            &o, (const void*)gemm_mfma_kernel<WF, BMT, EPI, TC, WQ>, 256, 0) != hipSuccess || o < 1)
       o = 1;
     occ = o;
   }
@@ -490,42 +421,43 @@ static hipError_t launch_persistent(const GemmArgs& a, int slots, hipStream_t s)
   const int nft = (a.N + 4 * WF - 1) / (4 * WF);
   const int max_items_per_xcd = ((slots + 7) / 8) * nft;
   const int wg_per_xcd = std::max(1, std::min(max_items_per_xcd, (cus / 8) * occ));
-  hipLaunchKernelGGL((gemm_mfma_kernel<WF, BMT, EPI, TC, PF>), dim3(8 * wg_per_xcd), dim3(256), 0,
+  hipLaunchKernelGGL((gemm_mfma_kernel<WF, BMT, EPI, TC, WQ>), dim3(8 * wg_per_xcd), dim3(256), 0,
                      s, a, nft, slots, wg_per_xcd);
   return hipGetLastError();
 }
 
-template <int WF, int BMT, int PF>
+template <int WF, int BMT, int WQ>
 static hipError_t launch_mfma_shape(const GemmArgs& a, int epi, bool tc_bf16, int slots,
                                     hipStream_t s) {
   if (tc_bf16) {
     switch (epi) {
-      case EPI_RELU2: return launch_persistent<WF, BMT, EPI_RELU2, bf16, PF>(a, slots, s);
-      case EPI_STORE: return launch_persistent<WF, BMT, EPI_STORE, bf16, PF>(a, slots, s);
-      case EPI_ADD_RES: return launch_persistent<WF, BMT, EPI_ADD_RES, bf16, PF>(a, slots, s);
+      case EPI_RELU2: return launch_persistent<WF, BMT, EPI_RELU2, bf16, WQ>(a, slots, s);
+      case EPI_STORE: return launch_persistent<WF, BMT, EPI_STORE, bf16, WQ>(a, slots, s);
+      case EPI_ADD_RES: return launch_persistent<WF, BMT, EPI_ADD_RES, bf16, WQ>(a, slots, s);
       default: return hipErrorInvalidValue;
     }
   }
   switch (epi) {
-    case EPI_RELU2: return launch_persistent<WF, BMT, EPI_RELU2, float, PF>(a, slots, s);
-    case EPI_STORE: return launch_persistent<WF, BMT, EPI_STORE, float, PF>(a, slots, s);
+    case EPI_RELU2: return launch_persistent<WF, BMT, EPI_RELU2, float, WQ>(a, slots, s);
+    case EPI_STORE: return launch_persistent<WF, BMT, EPI_STORE, float, WQ>(a, slots, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-#ifndef MOE_MFMA_PF
-#define MOE_MFMA_PF 1
-#endif
+template <int WQ>
+static hipError_t launch_mfma_wq(const GemmArgs& a, MfmaCfg cfg, int epi, bool tc_bf16, int slots,
+                                 hipStream_t s) {
+  if (cfg.wf == 16 && cfg.bmt == 16) return launch_mfma_shape<16, 16, WQ>(a, epi, tc_bf16, slots, s);
+  if (cfg.wf == 32 && cfg.bmt == 32) return launch_mfma_shape<32, 32, WQ>(a, epi, tc_bf16, slots, s);
+  if (cfg.wf == 32 && cfg.bmt == 64) return launch_mfma_shape<32, 64, WQ>(a, epi, tc_bf16, slots, s);
+  if (cfg.wf == 32 && cfg.bmt == 128) return launch_mfma_shape<32, 128, WQ>(a, epi, tc_bf16, slots, s);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_gemm_mfma(const GemmArgs& a, MfmaCfg cfg, int epi, bool tc_bf16, bool nvfp4,
                             int slots, hipStream_t s) {
-  if (nvfp4) return hipErrorInvalidValue;  // NVFP4 weights use their own kernel
-  constexpr int PF = MOE_MFMA_PF;
-  if (cfg.wf == 16 && cfg.bmt == 16) return launch_mfma_shape<16, 16, PF>(a, epi, tc_bf16, slots, s);
-  if (cfg.wf == 32 && cfg.bmt == 32) return launch_mfma_shape<32, 32, PF>(a, epi, tc_bf16, slots, s);
-  if (cfg.wf == 32 && cfg.bmt == 64) return launch_mfma_shape<32, 64, PF>(a, epi, tc_bf16, slots, s);
-  if (cfg.wf == 32 && cfg.bmt == 128) return launch_mfma_shape<32, 128, PF>(a, epi, tc_bf16, slots, s);
-  return hipErrorInvalidValue;
+  return nvfp4 ? launch_mfma_wq<1>(a, cfg, epi, tc_bf16, slots, s)
+               : launch_mfma_wq<0>(a, cfg, epi, tc_bf16, slots, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -554,5 +486,45 @@ hipError_t launch_retile_bf16(const bf16* src, bf16* dst, int G, int N, int K, h
   const size_t chunks = (size_t)G * N * K / 8;
   const int blocks = (int)std::min<size_t>((chunks + 255) / 256, 65536);
   hipLaunchKernelGGL(retile_bf16_kernel, dim3(blocks), dim3(256), 0, s, src, dst, G, N, K);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Re-tile NVFP4 [G][N][K/2] packed bytes and [G][N][K/16] E4M3 scales into the
+// lane order of the MFMA kernel: packed -> [G][N/16][K/64][64 lanes][8 bytes]
+// (lane l: row l%16; bytes 4*(l/16)..+3 and 16 + 4*(l/16)..+3 of the row's
+// 32-byte k-step), scales -> [G][N/16][K/64][16 rows][4 bytes].
+// ---------------------------------------------------------------------------
+__global__ void retile_nvfp4_kernel(const uint8_t* __restrict__ qsrc,
+                                    const uint8_t* __restrict__ ssrc, uint8_t* __restrict__ qdst,
+                                    uint8_t* __restrict__ sdst, int G, int N, int K) {
+  const int KS = K / 64, NT = N / 16;
+  const size_t lanes = (size_t)G * NT * KS * 64;
+  for (size_t c = blockIdx.x * (size_t)blockDim.x + threadIdx.x; c < lanes;
+       c += (size_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(c & 63);
+    size_t blk = c >> 6;  // (g, rt, ks)
+    const int ks = (int)(blk % KS);
+    blk /= KS;
+    const int rt = (int)(blk % NT);
+    const size_t g = blk / NT;
+    const int row = rt * 16 + (lane & 15);
+    const uint8_t* rq = qsrc + (g * N + row) * (size_t)(K / 2) + ks * 32 + 4 * (lane >> 4);
+    const uint32_t lo = *(const uint32_t*)rq;
+    const uint32_t hi = *(const uint32_t*)(rq + 16);
+    *(u32x2*)(qdst + c * 8) = u32x2{lo, hi};
+    if (lane < 16) {
+      const uint8_t* rs = ssrc + (g * N + rt * 16 + lane) * (size_t)(K / 16) + ks * 4;
+      *(uint32_t*)(sdst + ((blk * KS + ks) * 16 + lane) * 4) = *(const uint32_t*)rs;
+    }
+  }
+}
+
+hipError_t launch_retile_nvfp4(const uint8_t* qsrc, const uint8_t* ssrc, uint8_t* qdst,
+                               uint8_t* sdst, int G, int N, int K, hipStream_t s) {
+  const size_t lanes = (size_t)G * (N / 16) * (K / 64) * 64;
+  const int blocks = (int)std::min<size_t>((lanes + 255) / 256, 65536);
+  hipLaunchKernelGGL(retile_nvfp4_kernel, dim3(blocks), dim3(256), 0, s, qsrc, ssrc, qdst, sdst, G,
+                     N, K);
   return hipGetLastError();
 }

@@ -57,16 +57,16 @@ struct MfmaCfg {
   int wf;   // features per wave (16, 32, 64)
   int bmt;  // rows (tokens / routes) per workgroup tile (16, 32, 64, 128)
 };
+// `slots` = row tiles (grouped: tile-list capacity, live count read on device).
 hipError_t launch_gemm_mfma(const GemmArgs& a, MfmaCfg cfg, int epi, bool tc_bf16, bool nvfp4,
-                            int grid_y, hipStream_t s);
-
-// Barrier-free streaming grouped/dense GEMM for few rows per tile (wf, bmt in
-// {16,16}, {32,32}, {32,64}); `slots` row tiles (grouped: tile-list capacity).
-hipError_t launch_gemm_stream(const GemmArgs& a, MfmaCfg cfg, int epi, bool tc_bf16, int slots,
-                              hipStream_t s);
+                            int slots, hipStream_t s);
 
 // Re-tile bf16 [G][N][K] row-major weights into the MFMA lane order.
 hipError_t launch_retile_bf16(const bf16* src, bf16* dst, int G, int N, int K, hipStream_t s);
+
+// Re-tile NVFP4 [G][N][K/2] packed + [G][N][K/16] scales into the MFMA lane order.
+hipError_t launch_retile_nvfp4(const uint8_t* qsrc, const uint8_t* ssrc, uint8_t* qdst,
+                               uint8_t* sdst, int G, int N, int K, hipStream_t s);
 
 // Unpermute + weighted reduce (+ shared + residual in direct mode).
 //   direct: out[t] = residual[t] + sum_j w[t][j] * y[inv[t*k+j]] + sh[t]

@@ -31,10 +31,6 @@
 
 #include "kernels.h"
 
-#ifndef MOE_USE_STREAM_GEMM
-#define MOE_USE_STREAM_GEMM 0
-#endif
-
 namespace {
 
 thread_local std::string g_last_error;
@@ -73,6 +69,11 @@ struct moe_layer {
   void* down = nullptr;
   void* sh_up = nullptr;
   void* sh_down = nullptr;
+  // NVFP4 experts: re-tiled block scales and per-matrix scale2 (the packed
+  // nibbles live in up/down/sh_up/sh_down).
+  bool nvfp4 = false;
+  void *up_s = nullptr, *down_s = nullptr, *sh_up_s = nullptr, *sh_down_s = nullptr;
+  float *up_s2 = nullptr, *down_s2 = nullptr, *sh_up_s2 = nullptr, *sh_down_s2 = nullptr;
   // Workspace (max_tokens rows).
   void* normed = nullptr;
   float* logits = nullptr;
@@ -164,8 +165,6 @@ int check_config(const moe_layer_config_t& c) {
     return fail(MOE_ERR_INVALID_CONFIG, "bf16 activations need bf16 or NVFP4 experts");
   if (c.act_dtype != MOE_DT_F32 && c.act_dtype != MOE_DT_BF16)
     return fail(MOE_ERR_INVALID_CONFIG, "act_dtype=%d unsupported", c.act_dtype);
-  if (c.expert_dtype == MOE_DT_NVFP4)
-    return fail(MOE_ERR_INVALID_CONFIG, "NVFP4 experts are not built yet");
   const int q = f32 ? 16 : 64;
   const int dims[4] = {c.hidden_size, c.moe_inter, c.shared_inter, c.latent_size};
   const char* names[4] = {"hidden_size", "moe_inter", "shared_inter", "latent_size"};
@@ -198,6 +197,22 @@ int upload_proj(moe_layer* L, void** dst, const void* src, int G, int N, int K, 
   return MOE_OK;
 }
 
+// Copy an NVFP4 stack [G][N][K] (packed, scales, scale2) into layer memory,
+// re-tiled for the MFMA kernel.
+int upload_nvfp4(moe_layer* L, void** q, void** sc, float** s2, const moe_nvfp4_t& src, int G,
+                 int N, int K, hipStream_t s, const char* name) {
+  if (!src.packed || !src.scales || !src.scale2)
+    return fail(MOE_ERR_INVALID_ARG, "NVFP4 weight '%s' has a NULL pointer", name);
+  int rc = dalloc(L, q, (size_t)G * N * K / 2);
+  if (!rc) rc = dalloc(L, sc, (size_t)G * N * K / 16);
+  if (!rc) rc = dalloc(L, (void**)s2, (size_t)G * 4);
+  if (rc) return rc;
+  HIP_TRY(launch_retile_nvfp4((const uint8_t*)src.packed, (const uint8_t*)src.scales,
+                              (uint8_t*)*q, (uint8_t*)*sc, G, N, K, s));
+  HIP_TRY(hipMemcpyAsync(*s2, src.scale2, (size_t)G * 4, hipMemcpyDeviceToDevice, s));
+  return MOE_OK;
+}
+
 MfmaCfg grouped_cfg(int rows_per_group) {
   if (rows_per_group <= 16) return {16, 16};
   if (rows_per_group <= 32) return {32, 32};
@@ -215,22 +230,28 @@ MfmaCfg dense_cfg(int n) {
   return {32, 128};
 }
 
-int gemm(moe_layer* L, const GemmArgs& a, int epi, bool out_bf16, int bm_or_cfg_rows,
-         MfmaCfg cfg, int grid_y, hipStream_t s, const char* what) {
-  hipError_t e;
-  if (L->mfma) {
-#if MOE_USE_STREAM_GEMM
-    if (cfg.bmt <= 64)
-      e = launch_gemm_stream(a, cfg, epi, out_bf16, grid_y, s);
-    else
-#endif
-      e = launch_gemm_mfma(a, cfg, epi, out_bf16, false, grid_y, s);
-  } else {
-    (void)bm_or_cfg_rows;
-    e = launch_gemm_simt_f32(a, epi, grid_y, s);
-  }
+// One GEMM launch. `nvfp4` marks the expert projections of an NVFP4 layer;
+// the caller fills the NVFP4 fields of `a`.
+int gemm(moe_layer* L, const GemmArgs& a, int epi, bool out_bf16, MfmaCfg cfg, int slots,
+         hipStream_t s, const char* what, bool nvfp4 = false) {
+  hipError_t e = L->mfma ? launch_gemm_mfma(a, cfg, epi, out_bf16, nvfp4, slots, s)
+                         : launch_gemm_simt_f32(a, epi, slots, s);
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
   return MOE_OK;
+}
+
+// Set the weight operand of an expert projection (bf16/fp32 or NVFP4).
+void set_weights(const moe_layer* L, GemmArgs& a, const void* w, const void* sc, const float* s2,
+                 int N, int K) {
+  a.B = w;
+  if (L->nvfp4) {
+    a.b_gstride = (long long)N * K / 2;
+    a.b_scales = (const uint8_t*)sc;
+    a.bs_gstride = (long long)N * K / 16;
+    a.b_scale2 = s2;
+  } else {
+    a.b_gstride = (long long)N * K;
+  }
 }
 
 }  // namespace
@@ -272,8 +293,11 @@ int moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_weights_t* w
     }                                                                                  \
   } while (0)
 
-  if (!wts->norm_gamma || !wts->gate || !wts->up || !wts->down ||
-      (S > 0 && (!wts->shared_up || !wts->shared_down))) {
+  L->nvfp4 = c.expert_dtype == MOE_DT_NVFP4;
+  if (!wts->norm_gamma || !wts->gate ||
+      (!L->nvfp4 && (!wts->up || !wts->down || (S > 0 && (!wts->shared_up || !wts->shared_down)))) ||
+      (L->nvfp4 && (!wts->up_q.packed || !wts->down_q.packed ||
+                    (S > 0 && (!wts->shared_up_q.packed || !wts->shared_down_q.packed))))) {
     free_layer(L);
     return fail(MOE_ERR_INVALID_ARG, "a required weight (gamma, gate, up, down, shared) is NULL");
   }
@@ -291,11 +315,22 @@ int moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_weights_t* w
     TRY(upload_proj(L, &L->fc1, wts->fc1, 1, Lt, H, L->mfma, s, "fc1"));
     TRY(upload_proj(L, &L->fc2, wts->fc2, 1, H, Lt, L->mfma, s, "fc2"));
   }
-  TRY(upload_proj(L, &L->up, wts->up, E, I, D, L->mfma, s, "up"));
-  TRY(upload_proj(L, &L->down, wts->down, E, D, I, L->mfma, s, "down"));
-  if (S > 0) {
-    TRY(upload_proj(L, &L->sh_up, wts->shared_up, 1, S, H, L->mfma, s, "shared_up"));
-    TRY(upload_proj(L, &L->sh_down, wts->shared_down, 1, H, S, L->mfma, s, "shared_down"));
+  if (L->nvfp4) {
+    TRY(upload_nvfp4(L, &L->up, &L->up_s, &L->up_s2, wts->up_q, E, I, D, s, "up"));
+    TRY(upload_nvfp4(L, &L->down, &L->down_s, &L->down_s2, wts->down_q, E, D, I, s, "down"));
+    if (S > 0) {
+      TRY(upload_nvfp4(L, &L->sh_up, &L->sh_up_s, &L->sh_up_s2, wts->shared_up_q, 1, S, H, s,
+                       "shared_up"));
+      TRY(upload_nvfp4(L, &L->sh_down, &L->sh_down_s, &L->sh_down_s2, wts->shared_down_q, 1, H,
+                       S, s, "shared_down"));
+    }
+  } else {
+    TRY(upload_proj(L, &L->up, wts->up, E, I, D, L->mfma, s, "up"));
+    TRY(upload_proj(L, &L->down, wts->down, E, D, I, L->mfma, s, "down"));
+    if (S > 0) {
+      TRY(upload_proj(L, &L->sh_up, wts->shared_up, 1, S, H, L->mfma, s, "shared_up"));
+      TRY(upload_proj(L, &L->sh_down, wts->shared_down, 1, H, S, L->mfma, s, "shared_down"));
+    }
   }
   // Workspace.
   const size_t tiles_cap = R + (size_t)E + 1;  // >= sum_e ceil(c_e / bm) for any bm >= 1
@@ -367,17 +402,19 @@ int moe_layer_forward(moe_layer_t* L, void* hidden, void* residual, int32_t n, v
     {
       StageScope sc(L, MOE_STAGE_SHARED_UP, L->side);
       GemmArgs a{};
-      a.A = L->normed; a.lda = H; a.B = L->sh_up; a.C = L->g_sh; a.ldc = S;
+      a.A = L->normed; a.lda = H; a.C = L->g_sh; a.ldc = S;
       a.M = n; a.N = S; a.K = H;
-      int rc = gemm(L, a, EPI_RELU2, bf, dbmt, dc, dgrid, L->side, "shared up");
+      set_weights(L, a, L->sh_up, L->sh_up_s, L->sh_up_s2, S, H);
+      int rc = gemm(L, a, EPI_RELU2, bf, dc, dgrid, L->side, "shared up", L->nvfp4);
       if (rc) return rc;
     }
     {
       StageScope sc(L, MOE_STAGE_SHARED_DOWN, L->side);
       GemmArgs b{};
-      b.A = L->g_sh; b.lda = S; b.B = L->sh_down; b.C = L->sh; b.ldc = H;
+      b.A = L->g_sh; b.lda = S; b.C = L->sh; b.ldc = H;
       b.M = n; b.N = H; b.K = S;
-      int rc = gemm(L, b, EPI_STORE, false, dbmt, dc, dgrid, L->side, "shared down");
+      set_weights(L, b, L->sh_down, L->sh_down_s, L->sh_down_s2, H, S);
+      int rc = gemm(L, b, EPI_STORE, false, dc, dgrid, L->side, "shared down", L->nvfp4);
       if (rc) return rc;
     }
     HIP_TRY(hipEventRecord(L->ev_join, L->side));
@@ -390,7 +427,7 @@ int moe_layer_forward(moe_layer_t* L, void* hidden, void* residual, int32_t n, v
     GemmArgs a{};
     a.A = L->normed; a.lda = H; a.B = L->fc1; a.C = L->z; a.ldc = Lt;
     a.M = n; a.N = Lt; a.K = H;
-    int rc = gemm(L, a, EPI_STORE, bf, dbmt, dc, dgrid, s, "fc1");
+    int rc = gemm(L, a, EPI_STORE, bf, dc, dgrid, s, "fc1");
     if (rc) return rc;
     zin = L->z;
   }
@@ -414,20 +451,20 @@ int moe_layer_forward(moe_layer_t* L, void* hidden, void* residual, int32_t n, v
     StageScope sc(L, MOE_STAGE_GROUPED_UP, s);
     GemmArgs a{};
     a.A = zin; a.lda = D; a.a_rows = L->perm; a.a_div = k;
-    a.B = L->up; a.b_gstride = (long long)I * D;
+    set_weights(L, a, L->up, L->up_s, L->up_s2, I, D);
     a.C = L->h; a.ldc = I; a.N = I; a.K = D;
     a.tiles = L->tiles; a.num_tiles = L->num_tiles; a.offsets = L->offsets; a.bm = bm;
-    int rc = gemm(L, a, EPI_RELU2, bf, bm, gc, tiles_cap, s, "grouped up");
+    int rc = gemm(L, a, EPI_RELU2, bf, gc, tiles_cap, s, "grouped up", L->nvfp4);
     if (rc) return rc;
   }
   {
     StageScope sc(L, MOE_STAGE_GROUPED_DOWN, s);
     GemmArgs b{};
     b.A = L->h; b.lda = I;
-    b.B = L->down; b.b_gstride = (long long)D * I;
+    set_weights(L, b, L->down, L->down_s, L->down_s2, D, I);
     b.C = L->y; b.ldc = D; b.N = D; b.K = I;
     b.tiles = L->tiles; b.num_tiles = L->num_tiles; b.offsets = L->offsets; b.bm = bm;
-    int rc = gemm(L, b, EPI_STORE, false, bm, gc, tiles_cap, s, "grouped down");
+    int rc = gemm(L, b, EPI_STORE, false, gc, tiles_cap, s, "grouped down", L->nvfp4);
     if (rc) return rc;
   }
 
@@ -448,7 +485,7 @@ int moe_layer_forward(moe_layer_t* L, void* hidden, void* residual, int32_t n, v
     a.A = L->o; a.lda = Lt; a.B = L->fc2; a.C = hidden; a.ldc = H;
     a.M = n; a.N = H; a.K = Lt;
     a.res = residual; a.add = S > 0 ? L->sh : nullptr;
-    int rc = gemm(L, a, EPI_ADD_RES, bf, dbmt, dc, dgrid, s, "fc2");
+    int rc = gemm(L, a, EPI_ADD_RES, bf, dc, dgrid, s, "fc2");
     if (rc) return rc;
   }
   L->last_n = n;

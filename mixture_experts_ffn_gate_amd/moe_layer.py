@@ -133,8 +133,9 @@ class MoeLayer:
         self.act_dtype = act_dtype
         w = Weights()
         keep = []
-        for name in ("norm_gamma", "gate", "fc1", "fc2", "up", "down", "shared_up",
-                     "shared_down"):
+        dense_names = ("norm_gamma", "gate", "fc1", "fc2")
+        expert_names = ("up", "down", "shared_up", "shared_down")
+        for name in dense_names + (() if nvfp4 is not None else expert_names):
             key = "gamma" if name == "norm_gamma" else name
             t = weights.get(key)
             if t is not None:
@@ -227,9 +228,28 @@ def nvfp4_quantize(w: torch.Tensor, stream=None):
     return packed, scales, scale2
 
 
+def quantize_experts(weights: dict, stream=None) -> dict:
+    """NVFP4 triplets of the routed and shared expert stacks of ``weights``
+    (fp32 masters), quantized on the device by moe_nvfp4_quantize."""
+    out = {}
+    for key in ("up", "down", "shared_up", "shared_down"):
+        t = weights.get(key)
+        if t is None:
+            continue
+        t3 = t.float().contiguous()
+        if t3.dim() == 2:
+            t3 = t3.unsqueeze(0)
+        out[key] = nvfp4_quantize(t3, stream=stream)
+    return out
+
+
 def layer_from_workload(wl, weights: dict, max_tokens=None, nvfp4=None, stream=None) -> MoeLayer:
-    """Build a layer for a ``workloads.Workload`` from its weight dict."""
+    """Build a layer for a ``workloads.Workload`` from its weight dict (NVFP4
+    workloads quantize their fp32 expert masters with the library unless
+    ``nvfp4`` triplets are given)."""
     act = torch.float32 if wl.act_dtype == "f32" else torch.bfloat16
+    if wl.expert_dtype == "nvfp4" and nvfp4 is None:
+        nvfp4 = quantize_experts(weights, stream=stream)
     return MoeLayer(hidden_size=wl.H, num_experts=wl.E, top_k=wl.k, moe_inter=wl.I,
                     shared_inter=wl.S, latent_size=wl.L,
                     max_tokens=wl.N if max_tokens is None else max_tokens, weights=weights,

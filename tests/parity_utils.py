@@ -35,17 +35,39 @@ class LazyExperts:
         return self.cache[e]
 
 
-def oracle_weights(W: dict, nvfp4_q: dict | None = None, lazy_experts: bool = False) -> dict:
-    """Host weights for the oracle. NVFP4 layers pass the oracle's own
-    quantization of each projection in ``nvfp4_q`` (dequantized here)."""
+class LazyNvfp4Experts:
+    """Per-expert oracle NVFP4 quantize + dequantize of a device fp32 master
+    stack, computed on first use (the oracle's own encoder, never the GPU's)."""
+
+    def __init__(self, t: torch.Tensor):
+        self.t = t
+        self.cache = {}
+
+    def __getitem__(self, e):
+        e = int(e)
+        if e not in self.cache:
+            p, s, s2 = onv.quantize(wl_mod.to_numpy_f32(self.t[e]))
+            self.cache[e] = onv.dequantize(p, s, s2)
+        return self.cache[e]
+
+
+def oracle_weights(W: dict, nvfp4: bool = False, lazy_experts: bool = False) -> dict:
+    """Host weights for the oracle. For NVFP4 layers the expert and shared
+    projections are the oracle's own quantization of the fp32 masters,
+    dequantized (per expert on first use when ``lazy_experts``)."""
     out = {}
     for k, v in W.items():
-        if k in ("up", "down") and lazy_experts and nvfp4_q is None:
+        if nvfp4 and k in ("up", "down"):
+            if lazy_experts:
+                out[k] = LazyNvfp4Experts(v)
+            else:
+                p, s, s2 = onv.quantize_stack(wl_mod.to_numpy_f32(v))
+                out[k] = onv.dequantize_stack(p, s, s2)
+        elif nvfp4 and k in ("shared_up", "shared_down"):
+            p, s, s2 = onv.quantize(wl_mod.to_numpy_f32(v))
+            out[k] = onv.dequantize(p, s, s2)
+        elif k in ("up", "down") and lazy_experts:
             out[k] = LazyExperts(v)
-        elif nvfp4_q is not None and k in nvfp4_q:
-            p, s, s2 = nvfp4_q[k]
-            deq = onv.dequantize_stack(p, s, s2)
-            out[k] = deq if k in ("up", "down") else deq[0]
         else:
             out[k] = wl_mod.to_numpy_f32(v)
     return out

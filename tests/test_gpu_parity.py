@@ -289,6 +289,43 @@ def test_full_size_sampled(ml, name):
     print("errors", pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"], rows=rows))
 
 
+NVFP4_SMALL = {
+    "nvfp4_direct": wlm.Workload("nvfp4_direct_s", H=512, E=16, k=4, I=192, S=320, L=0, N=150,
+                                 expert_dtype="nvfp4"),
+    "nvfp4_latent": wlm.Workload("nvfp4_latent_s", H=512, E=8, k=2, I=256, S=256, L=128, N=70,
+                                 expert_dtype="nvfp4"),
+    "nvfp4_many_rows": wlm.Workload("nvfp4_many_rows", H=256, E=4, k=2, I=128, S=0, L=0, N=600,
+                                    expert_dtype="nvfp4"),
+}
+
+
+@pytest.mark.parametrize("name", list(NVFP4_SMALL))
+def test_small_nvfp4(ml, name):
+    wl = NVFP4_SMALL[name]
+    r = run_layer(ml, wl, wl.N, seed=7)
+    Wn = pu.oracle_weights(r["W"], nvfp4=True)
+    print("errors", pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"]))
+
+
+@pytest.mark.parametrize("n", [1, 5, 16])
+def test_small_nvfp4_decode_sizes(ml, n):
+    wl = NVFP4_SMALL["nvfp4_direct"]
+    r = run_layer(ml, wl, n, seed=8, max_tokens=64)
+    Wn = pu.oracle_weights(r["W"], nvfp4=True)
+    pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"])
+
+
+@pytest.mark.slow
+def test_full_size_nvfp4_sampled(ml):
+    wl = wlm.WORKLOADS["nvfp4_direct"]
+    r = run_layer(ml, wl, wl.N, seed=0)
+    Wn = pu.oracle_weights(r["W"], nvfp4=True, lazy_experts=True)
+    ref_ids, margin, _ = pu.oracle_routing(r["x"], Wn, wl)
+    pu.check_ids(r["ids"], ref_ids, margin)
+    rows = _sample_rows(wl.N, 4, 2)  # each sampled token quantizes its experts in the oracle
+    print("errors", pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"], rows=rows))
+
+
 @pytest.mark.parametrize("n", wlm.DECODE_NS)
 def test_decode_zipf_full(ml, n):
     wl = wlm.WORKLOADS["decode_zipf_bf16"]
