@@ -115,7 +115,7 @@ __global__ void __launch_bounds__(256) gemm_simt_f32_kernel(GemmArgs a) {
       if (EPI == EPI_RELU2) v = relu2(v);
       if (EPI == EPI_ADD_RES) {
         v += ((const float*)a.res)[(size_t)p * a.ldc + n];
-        if (a.add) v += a.add[(size_t)p * a.ldc + n];
+        if (a.add) v += ((const float*)a.add)[(size_t)p * a.ldc + n];
       }
       C[(size_t)p * a.ldc + n] = v;
     }
@@ -256,8 +256,8 @@ template <int FT> struct WSrc<1, FT> {
 // ---------------------------------------------------------------------------
 // Persistent MFMA GEMM (grouped or dense), WQ = 0 bf16 weights, 1 NVFP4.
 // ---------------------------------------------------------------------------
-template <int WF, int BMT, int EPI, typename TC, int WQ>
-__global__ void __launch_bounds__(256) gemm_mfma_kernel(GemmArgs a, int nft, int slots,
+template <int WF, int BMT, int EPI, typename TC, int WQ, bool GROUPED>
+__global__ void __launch_bounds__(256, (BMT >= 128 ? 2 : 1)) gemm_mfma_kernel(GemmArgs a, int nft, int slots,
                                                         int wg_per_xcd) {
   constexpr int FT = WF / 16;      // 16-feature tiles per wave
   constexpr int TT = BMT / 16;     // 16-row tiles per workgroup
@@ -277,14 +277,20 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(GemmArgs a, int nft, int
   // an XCD work on the feature tiles of the same row tiles (one expert's rows)
   // at the same time and the XCD's L2 fetches those activation rows once.
   const int xcd = blockIdx.x & 7;
-  const int live = a.tiles ? min(*a.num_tiles, slots) : slots;
+  const int live = GROUPED ? min(*a.num_tiles, slots) : slots;
   const int xslots = live > xcd ? (live - xcd + 7) / 8 : 0;
   const int items = xslots * nft;
   for (int item = blockIdx.x >> 3; item < items; item += wg_per_xcd) {
     const int slot = xcd + 8 * (item / nft);
     const int ftile = item % nft;
     TileInfo ti;
-    if (!decode_tile(a, slot, BMT, ti)) continue;
+    if (GROUPED) {
+      if (!decode_tile(a, slot, BMT, ti)) continue;
+    } else {
+      ti.g = 0;
+      ti.row0 = slot * BMT;
+      ti.rows = min(BMT, a.M - ti.row0);
+    }
 
     // Activation loader: chunk c = (tid + 256*i) % CHUNKS -> row c/8, 16-byte
     // chunk c%8 (small tiles: several threads load the same chunk, so every
@@ -296,7 +302,7 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(GemmArgs a, int nft, int
       const int c = (tid + 256 * i) % CHUNKS;
       const int row = c >> 3, ch = c & 7;
       const int r = min(row, ti.rows - 1);
-      const int arow = a_row_of(a, ti.row0 + r);
+      const int arow = GROUPED ? a_row_of(a, ti.row0 + r) : ti.row0 + r;
       asrc[i] = (const bf16*)a.A + (size_t)arow * a.lda + ch * 8;
       lds_off[i] = row * BK + ((ch ^ (row & 7)) << 3);
     }
@@ -390,7 +396,7 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(GemmArgs a, int nft, int
         }
         if (EPI == EPI_ADD_RES) {
           v += store4<TC>::ld((const TC*)a.res + (size_t)p * a.ldc + n);
-          if (a.add) v += *(const floatx4*)(a.add + (size_t)p * a.ldc + n);
+          if (a.add) v += store4<TC>::ld((const TC*)a.add + (size_t)p * a.ldc + n);
         }
         store4<TC>::st(C + (size_t)p * a.ldc + n, v);
       }
@@ -399,13 +405,15 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(GemmArgs a, int nft, int
   }
 }
 
-template <int WF, int BMT, int EPI, typename TC, int WQ>
+template <int WF, int BMT, int EPI, typename TC, int WQ, bool GROUPED>
 static hipError_t launch_persistent(const GemmArgs& a, int slots, hipStream_t s) {
   static int occ = 0;  // resident workgroups per CU (queried once per process)
   if (occ == 0) {
     int o = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &o, (const void*)gemm_mfma_kernel<WF, BMT, EPI, TC, WQ>, 256, 0) != hipSuccess || o < 1)
+            &o, (const void*)gemm_mfma_kernel<WF, BMT, EPI, TC, WQ, GROUPED>, 256, 0) !=
+            hipSuccess ||
+        o < 1)
       o = 1;
     occ = o;
   }
@@ -421,43 +429,45 @@ static hipError_t launch_persistent(const GemmArgs& a, int slots, hipStream_t s)
   const int nft = (a.N + 4 * WF - 1) / (4 * WF);
   const int max_items_per_xcd = ((slots + 7) / 8) * nft;
   const int wg_per_xcd = std::max(1, std::min(max_items_per_xcd, (cus / 8) * occ));
-  hipLaunchKernelGGL((gemm_mfma_kernel<WF, BMT, EPI, TC, WQ>), dim3(8 * wg_per_xcd), dim3(256), 0,
-                     s, a, nft, slots, wg_per_xcd);
+  hipLaunchKernelGGL((gemm_mfma_kernel<WF, BMT, EPI, TC, WQ, GROUPED>), dim3(8 * wg_per_xcd),
+                     dim3(256), 0, s, a, nft, slots, wg_per_xcd);
   return hipGetLastError();
 }
 
-template <int WF, int BMT, int WQ>
+template <int WF, int BMT, int WQ, bool G>
 static hipError_t launch_mfma_shape(const GemmArgs& a, int epi, bool tc_bf16, int slots,
                                     hipStream_t s) {
   if (tc_bf16) {
     switch (epi) {
-      case EPI_RELU2: return launch_persistent<WF, BMT, EPI_RELU2, bf16, WQ>(a, slots, s);
-      case EPI_STORE: return launch_persistent<WF, BMT, EPI_STORE, bf16, WQ>(a, slots, s);
-      case EPI_ADD_RES: return launch_persistent<WF, BMT, EPI_ADD_RES, bf16, WQ>(a, slots, s);
+      case EPI_RELU2: return launch_persistent<WF, BMT, EPI_RELU2, bf16, WQ, G>(a, slots, s);
+      case EPI_STORE: return launch_persistent<WF, BMT, EPI_STORE, bf16, WQ, G>(a, slots, s);
+      case EPI_ADD_RES:
+        if (G) return hipErrorInvalidValue;  // only the dense fc2 adds residual + shared
+        return launch_persistent<WF, BMT, EPI_ADD_RES, bf16, WQ, false>(a, slots, s);
       default: return hipErrorInvalidValue;
     }
   }
-  switch (epi) {
-    case EPI_RELU2: return launch_persistent<WF, BMT, EPI_RELU2, float, WQ>(a, slots, s);
-    case EPI_STORE: return launch_persistent<WF, BMT, EPI_STORE, float, WQ>(a, slots, s);
-    default: return hipErrorInvalidValue;
-  }
+  return hipErrorInvalidValue;  // bf16 layers keep every intermediate in bf16
 }
 
-template <int WQ>
+template <int WQ, bool G>
 static hipError_t launch_mfma_wq(const GemmArgs& a, MfmaCfg cfg, int epi, bool tc_bf16, int slots,
                                  hipStream_t s) {
-  if (cfg.wf == 16 && cfg.bmt == 16) return launch_mfma_shape<16, 16, WQ>(a, epi, tc_bf16, slots, s);
-  if (cfg.wf == 32 && cfg.bmt == 32) return launch_mfma_shape<32, 32, WQ>(a, epi, tc_bf16, slots, s);
-  if (cfg.wf == 32 && cfg.bmt == 64) return launch_mfma_shape<32, 64, WQ>(a, epi, tc_bf16, slots, s);
-  if (cfg.wf == 32 && cfg.bmt == 128) return launch_mfma_shape<32, 128, WQ>(a, epi, tc_bf16, slots, s);
+  if (cfg.wf == 16 && cfg.bmt == 16) return launch_mfma_shape<16, 16, WQ, G>(a, epi, tc_bf16, slots, s);
+  if (cfg.wf == 32 && cfg.bmt == 32) return launch_mfma_shape<32, 32, WQ, G>(a, epi, tc_bf16, slots, s);
+  if (cfg.wf == 32 && cfg.bmt == 64) return launch_mfma_shape<32, 64, WQ, G>(a, epi, tc_bf16, slots, s);
+  if (cfg.wf == 32 && cfg.bmt == 128) return launch_mfma_shape<32, 128, WQ, G>(a, epi, tc_bf16, slots, s);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm_mfma(const GemmArgs& a, MfmaCfg cfg, int epi, bool tc_bf16, bool nvfp4,
                             int slots, hipStream_t s) {
-  return nvfp4 ? launch_mfma_wq<1>(a, cfg, epi, tc_bf16, slots, s)
-               : launch_mfma_wq<0>(a, cfg, epi, tc_bf16, slots, s);
+  const bool g = a.tiles != nullptr;
+  if (nvfp4)
+    return g ? launch_mfma_wq<1, true>(a, cfg, epi, tc_bf16, slots, s)
+             : launch_mfma_wq<1, false>(a, cfg, epi, tc_bf16, slots, s);
+  return g ? launch_mfma_wq<0, true>(a, cfg, epi, tc_bf16, slots, s)
+           : launch_mfma_wq<0, false>(a, cfg, epi, tc_bf16, slots, s);
 }
 
 // ---------------------------------------------------------------------------

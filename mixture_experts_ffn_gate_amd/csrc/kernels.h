@@ -5,12 +5,13 @@
 #include "../../include/moe_layer.h"
 
 #define MOE_MAX_E 512
+#define MOE_MAX_TOPK_REDUCE 16  // = MOE_MAX_TOP_K
 
 // Epilogues of the GEMM kernels.
 enum {
   EPI_RELU2 = 0,    // C = relu(acc)^2
   EPI_STORE = 1,    // C = acc
-  EPI_ADD_RES = 2   // C = acc + res + add   (res in C's dtype, add fp32 or null)
+  EPI_ADD_RES = 2   // C = acc + res + add   (res, add in C's dtype; add may be null)
 };
 
 // One GEMM launch: C[p][n] = sum_k A[arow(p)][k] * B[g][n][k], then the epilogue.
@@ -37,7 +38,7 @@ struct GemmArgs {
   const int* offsets;
   int bm;
   const void* res;
-  const float* add;
+  const void* add;  // EPI_ADD_RES second addend, C's dtype (may be null)
 };
 
 hipError_t launch_norm_gate(int act_dt, const void* hidden, const void* gamma, const void* wgate,
@@ -68,12 +69,13 @@ hipError_t launch_retile_bf16(const bf16* src, bf16* dst, int G, int N, int K, h
 hipError_t launch_retile_nvfp4(const uint8_t* qsrc, const uint8_t* ssrc, uint8_t* qdst,
                                uint8_t* sdst, int G, int N, int K, hipStream_t s);
 
-// Unpermute + weighted reduce (+ shared + residual in direct mode).
+// Unpermute + weighted reduce (+ shared + residual in direct mode). y, residual,
+// sh and out are in the activation dtype `dt`; sums run in fp32.
 //   direct: out[t] = residual[t] + sum_j w[t][j] * y[inv[t*k+j]] + sh[t]
 //   latent: out[t] = sum_j w[t][j] * y[inv[t*k+j]]      (res, sh unused)
-hipError_t launch_unpermute_reduce(int out_dt, bool latent, const float* y, const int* inv,
+hipError_t launch_unpermute_reduce(int dt, bool latent, const void* y, const int* inv,
                                    const float* w, int n, int k, int D, const void* residual,
-                                   const float* sh, void* out, hipStream_t s);
+                                   const void* sh, void* out, hipStream_t s);
 
 hipError_t launch_nvfp4_quantize(const float* w, int G, int rows, int cols, uint8_t* packed,
                                  uint8_t* scales, float* scale2, hipStream_t s);

@@ -86,10 +86,10 @@ struct moe_layer {
   int2* tiles = nullptr;
   int* num_tiles = nullptr;
   void* g_sh = nullptr;   // shared-expert activation [N][S]
-  float* sh = nullptr;    // shared-expert output fp32 [N][H]
+  void* sh = nullptr;     // shared-expert output [N][H]
   void* z = nullptr;      // latent input [N][L]
   void* h = nullptr;      // routed activation [R][I]
-  float* y = nullptr;     // routed output fp32 [R][D]
+  void* y = nullptr;      // routed output [R][D], expert-sorted rows
   void* o = nullptr;      // latent routed sum [N][L]
   std::vector<void*> allocs;
   hipStream_t side = nullptr;
@@ -221,7 +221,7 @@ MfmaCfg grouped_cfg(int rows_per_group) {
 }
 
 #ifndef MOE_DENSE_BMT
-#define MOE_DENSE_BMT 64
+#define MOE_DENSE_BMT 128
 #endif
 MfmaCfg dense_cfg(int n) {
   if (n <= 16) return {16, 16};
@@ -346,14 +346,14 @@ int moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_weights_t* w
   TRY(dalloc(L, (void**)&L->num_tiles, 16));
   if (S > 0) {
     TRY(dalloc(L, &L->g_sh, (size_t)N * S * as));
-    TRY(dalloc(L, (void**)&L->sh, (size_t)N * H * 4));
+    TRY(dalloc(L, &L->sh, (size_t)N * H * as));
   }
   if (Lt > 0) {
     TRY(dalloc(L, &L->z, (size_t)N * Lt * as));
     TRY(dalloc(L, &L->o, (size_t)N * Lt * as));
   }
   TRY(dalloc(L, &L->h, R * I * as));
-  TRY(dalloc(L, (void**)&L->y, R * D * 4));
+  TRY(dalloc(L, &L->y, R * D * as));
 
   TRYH(hipStreamCreateWithFlags(&L->side, hipStreamNonBlocking));
   TRYH(hipEventCreateWithFlags(&L->ev_fork, hipEventDisableTiming));
@@ -414,7 +414,7 @@ int moe_layer_forward(moe_layer_t* L, void* hidden, void* residual, int32_t n, v
       b.A = L->g_sh; b.lda = S; b.C = L->sh; b.ldc = H;
       b.M = n; b.N = H; b.K = S;
       set_weights(L, b, L->sh_down, L->sh_down_s, L->sh_down_s2, H, S);
-      int rc = gemm(L, b, EPI_STORE, false, dc, dgrid, L->side, "shared down", L->nvfp4);
+      int rc = gemm(L, b, EPI_STORE, bf, dc, dgrid, L->side, "shared down", L->nvfp4);
       if (rc) return rc;
     }
     HIP_TRY(hipEventRecord(L->ev_join, L->side));
@@ -464,7 +464,7 @@ int moe_layer_forward(moe_layer_t* L, void* hidden, void* residual, int32_t n, v
     set_weights(L, b, L->down, L->down_s, L->down_s2, D, I);
     b.C = L->y; b.ldc = D; b.N = D; b.K = I;
     b.tiles = L->tiles; b.num_tiles = L->num_tiles; b.offsets = L->offsets; b.bm = bm;
-    int rc = gemm(L, b, EPI_STORE, false, gc, tiles_cap, s, "grouped down", L->nvfp4);
+    int rc = gemm(L, b, EPI_STORE, bf, gc, tiles_cap, s, "grouped down", L->nvfp4);
     if (rc) return rc;
   }
 

@@ -6,52 +6,77 @@
 //
 // The routed rows y are in expert-sorted order; row inv[t*k + j] holds slot j
 // of token t. Slots are summed in slot order (no atomics), so the result is
-// deterministic. Each thread owns 4 consecutive columns: 16-byte loads of y.
+// deterministic. Each thread owns 4 consecutive columns; the k slot indices
+// and weights are loaded first so that the k row loads issue together.
 #include "kernels.h"
 
-template <typename TO, bool LATENT>
+template <typename T> struct vec4;
+template <> struct vec4<float> {
+  static __device__ __forceinline__ floatx4 ld(const float* p) { return *(const floatx4*)p; }
+  static __device__ __forceinline__ void st(float* p, floatx4 v) { *(floatx4*)p = v; }
+};
+template <> struct vec4<bf16> {
+  static __device__ __forceinline__ floatx4 ld(const bf16* p) {
+    const bf16x4 i = *(const bf16x4*)p;
+    return floatx4{(float)i[0], (float)i[1], (float)i[2], (float)i[3]};
+  }
+  static __device__ __forceinline__ void st(bf16* p, floatx4 v) {
+    bf16x4 o;
+    o[0] = (bf16)v[0]; o[1] = (bf16)v[1]; o[2] = (bf16)v[2]; o[3] = (bf16)v[3];
+    *(bf16x4*)p = o;
+  }
+};
+
+template <typename T, bool LATENT>
 __global__ void __launch_bounds__(256) unpermute_reduce_kernel(
-    const float* __restrict__ y, const int* __restrict__ inv, const float* __restrict__ w, int n,
-    int k, int D, const TO* __restrict__ residual, const float* __restrict__ sh,
-    TO* __restrict__ out) {
+    const T* __restrict__ y, const int* __restrict__ inv, const float* __restrict__ w, int n,
+    int k, int D, const T* __restrict__ residual, const T* __restrict__ sh, T* __restrict__ out) {
   const int t = blockIdx.x;
   const int d = (blockIdx.y * 256 + threadIdx.x) * 4;
   if (t >= n || d >= D) return;
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const int p = inv[t * k + j];
-    const float wt = w[t * k + j];
-    const floatx4 v = *(const floatx4*)(y + (size_t)p * D + d);
-    acc += wt * v;
-  }
+  int p[MOE_MAX_TOPK_REDUCE];
+  float wt[MOE_MAX_TOPK_REDUCE];
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK_REDUCE; ++j)
+    if (j < k) {
+      p[j] = inv[t * k + j];
+      wt[j] = w[t * k + j];
+    }
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK_REDUCE; ++j)
+    if (j < k) acc += wt[j] * vec4<T>::ld(y + (size_t)p[j] * D + d);
   const size_t o = (size_t)t * D + d;
   if (!LATENT) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) acc[q] = io<TO>::ld(residual + o + q) + acc[q];
-    if (sh) acc += *(const floatx4*)(sh + o);
+    acc = vec4<T>::ld(residual + o) + acc;
+    if (sh) acc += vec4<T>::ld(sh + o);
   }
-#pragma unroll
-  for (int q = 0; q < 4; ++q) io<TO>::st(out + o + q, acc[q]);
+  vec4<T>::st(out + o, acc);
 }
 
-hipError_t launch_unpermute_reduce(int out_dt, bool latent, const float* y, const int* inv,
+hipError_t launch_unpermute_reduce(int dt, bool latent, const void* y, const int* inv,
                                    const float* w, int n, int k, int D, const void* residual,
-                                   const float* sh, void* out, hipStream_t s) {
+                                   const void* sh, void* out, hipStream_t s) {
+  if (k > MOE_MAX_TOPK_REDUCE) return hipErrorInvalidValue;
   dim3 grid(n, (D / 4 + 255) / 256);
-  if (out_dt == MOE_DT_BF16) {
+  if (dt == MOE_DT_BF16) {
     if (latent)
-      hipLaunchKernelGGL((unpermute_reduce_kernel<bf16, true>), grid, dim3(256), 0, s, y, inv, w, n,
-                         k, D, (const bf16*)residual, sh, (bf16*)out);
+      hipLaunchKernelGGL((unpermute_reduce_kernel<bf16, true>), grid, dim3(256), 0, s,
+                         (const bf16*)y, inv, w, n, k, D, (const bf16*)residual, (const bf16*)sh,
+                         (bf16*)out);
     else
-      hipLaunchKernelGGL((unpermute_reduce_kernel<bf16, false>), grid, dim3(256), 0, s, y, inv, w,
-                         n, k, D, (const bf16*)residual, sh, (bf16*)out);
+      hipLaunchKernelGGL((unpermute_reduce_kernel<bf16, false>), grid, dim3(256), 0, s,
+                         (const bf16*)y, inv, w, n, k, D, (const bf16*)residual, (const bf16*)sh,
+                         (bf16*)out);
   } else {
     if (latent)
-      hipLaunchKernelGGL((unpermute_reduce_kernel<float, true>), grid, dim3(256), 0, s, y, inv, w,
-                         n, k, D, (const float*)residual, sh, (float*)out);
+      hipLaunchKernelGGL((unpermute_reduce_kernel<float, true>), grid, dim3(256), 0, s,
+                         (const float*)y, inv, w, n, k, D, (const float*)residual,
+                         (const float*)sh, (float*)out);
     else
-      hipLaunchKernelGGL((unpermute_reduce_kernel<float, false>), grid, dim3(256), 0, s, y, inv, w,
-                         n, k, D, (const float*)residual, sh, (float*)out);
+      hipLaunchKernelGGL((unpermute_reduce_kernel<float, false>), grid, dim3(256), 0, s,
+                         (const float*)y, inv, w, n, k, D, (const float*)residual,
+                         (const float*)sh, (float*)out);
   }
   return hipGetLastError();
 }

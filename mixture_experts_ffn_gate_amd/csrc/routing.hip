@@ -127,22 +127,37 @@ __global__ void __launch_bounds__(256) norm_gate_mfma_kernel(const bf16* __restr
   const int t0 = blockIdx.x * 16;
   const int e0 = blockIdx.y * ET * 16;
 
-  // 1. inverse RMS (each wave: rows wave*4 .. +3; 16-byte loads)
-  for (int t = wave * 4; t < wave * 4 + 4; ++t) {
-    float ss = 0.f;
-    if (t0 + t < n) {
-      const bf16* x = hidden + (size_t)(t0 + t) * H;
-      for (int i = lane * 8; i < H; i += 512) {
-        const bf16x8 v = *(const bf16x8*)(x + i);
+  // 1. inverse RMS (each wave: rows wave*4 .. +3; the 16-byte loads of all
+  //    four rows are issued together, 4 chunks per row at a time).
+  {
+    float ss[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int i0 = lane * 8; i0 < H; i0 += 512 * 4) {
+      bf16x8 v[4][4];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float f = (float)v[q];
-          ss += f * f;
+      for (int r = 0; r < 4; ++r) {
+        const int t = wave * 4 + r;
+        const bf16* x = hidden + (size_t)min(t0 + t, n - 1) * H;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + u * 512;
+          v[r][u] = i < H ? *(const bf16x8*)(x + i) : bf16x8{};
         }
       }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const float f = (float)v[r][u][q];
+            ss[r] += f * f;
+          }
     }
-    ss = wave_sum(ss);
-    if (lane == 0) rinv[t] = 1.0f / sqrtf(ss / (float)H + eps);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float tot = wave_sum(ss[r]);
+      if (lane == 0) rinv[wave * 4 + r] = 1.0f / sqrtf(tot / (float)H + eps);
+    }
   }
   __syncthreads();
 
@@ -161,29 +176,39 @@ __global__ void __launch_bounds__(256) norm_gate_mfma_kernel(const bf16* __restr
 #pragma unroll
   for (int et = 0; et < ET; ++et) acc[et] = floatx4{0.f, 0.f, 0.f, 0.f};
   const size_t row = (size_t)(t0 + tok) * H + kg * 8;
-  for (int k0 = wave * 32; k0 < H; k0 += 128) {
-    bf16x8 wf[ET];
+  // Four k-steps per round: their loads are issued before any of them is used.
+  constexpr int U = 4;
+  for (int kb = wave * 32; kb < H; kb += 128 * U) {
+    bf16x8 wf[U][ET], xv[U], gv[U];
 #pragma unroll
-    for (int et = 0; et < ET; ++et) wf[et] = *(const bf16x8*)(wbase[et] + k0);
-    bf16x8 xv = {};
-    if (tvalid) xv = *(const bf16x8*)(hidden + row + k0);
-    const bf16x8 gv = *(const bf16x8*)(gamma + k0 + kg * 8);
-    bf16x8 hi, lo, nb;
+    for (int u = 0; u < U; ++u) {
+      const int k0 = min(kb + u * 128, H - 32);  // past the end: a valid step, not used
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const float v = (float)xv[q] * rv * (float)gv[q];
-      hi[q] = (bf16)v;
-      lo[q] = (bf16)(v - (float)hi[q]);
-      nb[q] = hi[q];
-    }
-    if (writer && tvalid) {
-      *(bf16x8*)(residual + row + k0) = xv;
-      *(bf16x8*)(normed + row + k0) = nb;
+      for (int et = 0; et < ET; ++et) wf[u][et] = *(const bf16x8*)(wbase[et] + k0);
+      xv[u] = tvalid ? *(const bf16x8*)(hidden + row + k0) : bf16x8{};
+      gv[u] = *(const bf16x8*)(gamma + k0 + kg * 8);
     }
 #pragma unroll
-    for (int et = 0; et < ET; ++et) {
-      acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[et], hi, acc[et], 0, 0, 0);
-      acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[et], lo, acc[et], 0, 0, 0);
+    for (int u = 0; u < U; ++u) {
+      const int k0 = kb + u * 128;
+      if (k0 >= H) break;
+      bf16x8 hi, lo, nb;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float v = (float)xv[u][q] * rv * (float)gv[u][q];
+        hi[q] = (bf16)v;
+        lo[q] = (bf16)(v - (float)hi[q]);
+        nb[q] = hi[q];
+      }
+      if (writer && tvalid) {
+        *(bf16x8*)(residual + row + k0) = xv[u];
+        *(bf16x8*)(normed + row + k0) = nb;
+      }
+#pragma unroll
+      for (int et = 0; et < ET; ++et) {
+        acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u][et], hi, acc[et], 0, 0, 0);
+        acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u][et], lo, acc[et], 0, 0, 0);
+      }
     }
   }
 #pragma unroll
@@ -269,6 +294,15 @@ __global__ void __launch_bounds__(256) topk_sigmoid_kernel(const float* __restri
 //            within an expert: the order is stable and deterministic.
 // Ids outside [0, E) are skipped (they get no position).
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o, WAVE);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
 __global__ void __launch_bounds__(1024) route_sort_kernel(const int* __restrict__ ids, int R,
                                                           int E, int* __restrict__ counts,
                                                           int* __restrict__ offsets,
@@ -276,87 +310,108 @@ __global__ void __launch_bounds__(1024) route_sort_kernel(const int* __restrict_
                                                           int* __restrict__ inv, int bm,
                                                           int2* __restrict__ tiles,
                                                           int* __restrict__ num_tiles) {
+  constexpr int RPT = 16;  // routes per thread loaded per batch (one load latency)
   __shared__ int cnt[MOE_MAX_E];
   __shared__ int base[MOE_MAX_E];
-  __shared__ int tbase[MOE_MAX_E];
   __shared__ int wcnt[16][MOE_MAX_E];
-  __shared__ int scan_tmp[2][1024];
+  __shared__ int wsum[2][16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   for (int e = tid; e < MOE_MAX_E; e += 1024) {
     cnt[e] = 0;
+#pragma unroll
     for (int w = 0; w < 16; ++w) wcnt[w][e] = 0;
   }
   __syncthreads();
-  for (int r = tid; r < R; r += 1024) {
-    int e = ids[r];
-    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  // 1. histogram
+  for (int b0 = 0; b0 < R; b0 += 1024 * RPT) {
+    int ev[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int r = b0 + i * 1024 + tid;
+      ev[i] = r < R ? ids[r] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+      if (ev[i] >= 0 && ev[i] < E) atomicAdd(&cnt[ev[i]], 1);
   }
   __syncthreads();
 
-  // Exclusive scans over experts of counts and of tile counts (E <= 512 < 1024).
-  int c = tid < E ? cnt[tid] : 0;
-  int tc = (tid < E && bm > 0) ? (c + bm - 1) / bm : 0;
-  scan_tmp[0][tid] = c;
-  scan_tmp[1][tid] = tc;
+  // 2. exclusive scans over experts of counts and tile counts (E <= 512:
+  //    threads 0..511, 8 waves; wave-level shuffles, then the wave totals).
+  const int c = tid < E ? cnt[tid] : 0;
+  const int tc = (tid < E && bm > 0) ? (c + bm - 1) / bm : 0;
+  const int ic = wave_incl_scan(c, lane), itc = wave_incl_scan(tc, lane);
+  if (lane == 63) {
+    wsum[0][wave] = ic;
+    wsum[1][wave] = itc;
+  }
   __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    int a = tid >= off ? scan_tmp[0][tid - off] : 0;
-    int b = tid >= off ? scan_tmp[1][tid - off] : 0;
-    __syncthreads();
-    scan_tmp[0][tid] += a;
-    scan_tmp[1][tid] += b;
-    __syncthreads();
+  int pc = 0, ptc = 0;
+  for (int w = 0; w < wave; ++w) {
+    pc += wsum[0][w];
+    ptc += wsum[1][w];
   }
   if (tid < E) {
-    int excl = scan_tmp[0][tid] - c;
-    int texcl = scan_tmp[1][tid] - tc;
+    const int excl = pc + ic - c;
+    const int texcl = ptc + itc - tc;
     base[tid] = excl;
-    tbase[tid] = texcl;
     counts[tid] = c;
     offsets[tid] = excl;
     if (tid == E - 1) {
-      offsets[E] = scan_tmp[0][tid];
-      if (num_tiles) *num_tiles = scan_tmp[1][tid];
+      offsets[E] = excl + c;
+      if (num_tiles) *num_tiles = texcl + tc;
     }
     if (tiles)
       for (int i = 0; i < tc; ++i) tiles[texcl + i] = make_int2(tid, i * bm);
   }
   __syncthreads();
 
+  // 3. stable scatter, chunks of 1024 routes in order
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int c0 = 0; c0 < R; c0 += 1024) {
-    const int r = c0 + tid;
-    int e = r < R ? ids[r] : -1;
-    const bool valid = e >= 0 && e < E;
-    if (!valid) e = -1;
-    uint64_t mask = __ballot(valid);
+  for (int b0 = 0; b0 < R; b0 += 1024 * RPT) {
+    int ev[RPT];
 #pragma unroll
-    for (int b = 0; b < 10; ++b) {  // 10 bits cover E <= 1024
-      const bool bit = valid && ((e >> b) & 1);
-      const uint64_t bal = __ballot(bit);
-      mask &= bit ? bal : ~bal;
+    for (int i = 0; i < RPT; ++i) {
+      const int r = b0 + i * 1024 + tid;
+      ev[i] = r < R ? ids[r] : -1;
     }
-    const int rank = __popcll(mask & below);
-    if (valid && rank == 0) wcnt[wave][e] = __popcll(mask);
-    __syncthreads();
-    if (valid) {
-      int pre = 0;
-      for (int w = 0; w < wave; ++w) pre += wcnt[w][e];
-      const int pos = base[e] + pre + rank;
-      perm[pos] = r;
-      inv[r] = pos;
-    }
-    __syncthreads();
-    for (int ee = tid; ee < E; ee += 1024) {
-      int s = 0;
-      for (int w = 0; w < 16; ++w) {
-        s += wcnt[w][ee];
-        wcnt[w][ee] = 0;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int c0 = b0 + i * 1024;
+      if (c0 >= R) break;  // uniform across the block
+      const int r = c0 + tid;
+      const bool valid = ev[i] >= 0 && ev[i] < E;
+      const int e = valid ? ev[i] : -1;
+      uint64_t mask = __ballot(valid);
+#pragma unroll
+      for (int b = 0; b < 10; ++b) {  // 10 bits cover E <= 1024
+        const bool bit = valid && ((e >> b) & 1);
+        const uint64_t bal = __ballot(bit);
+        mask &= bit ? bal : ~bal;
       }
-      base[ee] += s;
+      const int rank = __popcll(mask & below);
+      if (valid && rank == 0) wcnt[wave][e] = __popcll(mask);
+      __syncthreads();
+      if (valid) {
+        int pre = 0;
+        for (int w = 0; w < wave; ++w) pre += wcnt[w][e];
+        const int pos = base[e] + pre + rank;
+        perm[pos] = r;
+        inv[r] = pos;
+      }
+      __syncthreads();
+      for (int ee = tid; ee < E; ee += 1024) {
+        int sum = 0;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) {
+          sum += wcnt[w][ee];
+          wcnt[w][ee] = 0;
+        }
+        base[ee] += sum;
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
 }
 
