@@ -201,24 +201,30 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t q, float sc) {
 //    step); scale2 of the group multiplies the accumulator in the epilogue.
 template <int WQ, int FT> struct WSrc;
 
+// Dead tiles (features past N, possible in the last feature tile) keep the
+// loads unconditional but point every lane at one fixed 16-byte chunk with a
+// zero step: one cached line instead of a re-read of live weights.
 template <int FT> struct WSrc<0, FT> {
   struct Frag { bf16x8 v[FT][2]; };
   const bf16* p[FT];
+  int step[FT];  // elements per 64-wide k-step (0 for a dead tile)
   __device__ __forceinline__ void init(const GemmArgs& a, int g, int nf0, int lane) {
     const bf16* W = (const bf16*)a.B + (size_t)g * a.b_gstride;
     const int KC = a.K / 32;
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) {
-      int rt = (nf0 >> 4) + ft;
-      if (rt * 16 >= a.N) rt = 0;  // dead tile: read valid memory, never stored
-      p[ft] = W + ((size_t)rt * KC * 64 + lane) * 8;
+      const int rt = (nf0 >> 4) + ft;
+      const bool live = rt * 16 < a.N;
+      p[ft] = live ? W + ((size_t)rt * KC * 64 + lane) * 8 : W;
+      step[ft] = live ? 1024 : 0;
     }
   }
   __device__ __forceinline__ void load(Frag& f, int ks) const {
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
-      for (int s = 0; s < 2; ++s) f.v[ft][s] = ld_stream((const bf16x8*)(p[ft] + ((size_t)ks * 2 + s) * 512));
+      for (int s = 0; s < 2; ++s)
+        f.v[ft][s] = ld_stream((const bf16x8*)(p[ft] + (size_t)ks * step[ft] + s * (step[ft] >> 1)));
   }
   __device__ __forceinline__ bf16x8 get(const Frag& f, int ft, int s, int) const { return f.v[ft][s]; }
 };
@@ -227,23 +233,24 @@ template <int FT> struct WSrc<1, FT> {
   struct Frag { u32x2 q[FT]; uint32_t sc[FT]; };
   const u32x2* pq[FT];
   const uint32_t* ps[FT];
+  int live[FT];  // 1 for a live tile, 0 for a dead one (fixed address, zero step)
   __device__ __forceinline__ void init(const GemmArgs& a, int g, int nf0, int lane) {
     const uint8_t* Q = (const uint8_t*)a.B + (size_t)g * a.b_gstride;
     const uint8_t* S = a.b_scales + (size_t)g * a.bs_gstride;
     const int KS = a.K / 64;
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) {
-      int rt = (nf0 >> 4) + ft;
-      if (rt * 16 >= a.N) rt = 0;
-      pq[ft] = (const u32x2*)Q + (size_t)rt * KS * 64 + lane;
-      ps[ft] = (const uint32_t*)S + (size_t)rt * KS * 16 + (lane & 15);
+      const int rt = (nf0 >> 4) + ft;
+      live[ft] = rt * 16 < a.N;
+      pq[ft] = (const u32x2*)Q + (live[ft] ? (size_t)rt * KS * 64 + lane : 0);
+      ps[ft] = (const uint32_t*)S + (live[ft] ? (size_t)rt * KS * 16 + (lane & 15) : 0);
     }
   }
   __device__ __forceinline__ void load(Frag& f, int ks) const {
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) {
-      f.q[ft] = ld_stream(pq[ft] + (size_t)ks * 64);
-      f.sc[ft] = ps[ft][(size_t)ks * 16];
+      f.q[ft] = ld_stream(pq[ft] + (size_t)ks * 64 * live[ft]);
+      f.sc[ft] = ps[ft][(size_t)ks * 16 * live[ft]];
     }
   }
   __device__ __forceinline__ bf16x8 get(const Frag& f, int ft, int s, int lane) const {
@@ -276,13 +283,18 @@ __global__ void __launch_bounds__(256, (BMT >= 128 ? 2 : 1)) gemm_mfma_kernel(Ge
   // the XCD's workgroup count. Items are row-tile major, so the workgroups of
   // an XCD work on the feature tiles of the same row tiles (one expert's rows)
   // at the same time and the XCD's L2 fetches those activation rows once.
+  //   Dense launches (one weight matrix reused by every row tile) deal the
+  // feature tiles to the XCDs instead: XCD x takes feature tiles x + 8*j and
+  // walks all row tiles of each, so each XCD's L2 holds only its own columns
+  // of the weight matrix.
   const int xcd = blockIdx.x & 7;
   const int live = GROUPED ? min(*a.num_tiles, slots) : slots;
   const int xslots = live > xcd ? (live - xcd + 7) / 8 : 0;
-  const int items = xslots * nft;
+  const int xft = nft > xcd ? (nft - xcd + 7) / 8 : 0;
+  const int items = GROUPED ? xslots * nft : xft * slots;
   for (int item = blockIdx.x >> 3; item < items; item += wg_per_xcd) {
-    const int slot = xcd + 8 * (item / nft);
-    const int ftile = item % nft;
+    const int slot = GROUPED ? xcd + 8 * (item / nft) : item % slots;
+    const int ftile = GROUPED ? item % nft : xcd + 8 * (item / slots);
     TileInfo ti;
     if (GROUPED) {
       if (!decode_tile(a, slot, BMT, ti)) continue;
@@ -427,7 +439,7 @@ static hipError_t launch_persistent(const GemmArgs& a, int slots, hipStream_t s)
     cus = n;
   }
   const int nft = (a.N + 4 * WF - 1) / (4 * WF);
-  const int max_items_per_xcd = ((slots + 7) / 8) * nft;
+  const int max_items_per_xcd = GROUPED ? ((slots + 7) / 8) * nft : ((nft + 7) / 8) * slots;
   const int wg_per_xcd = std::max(1, std::min(max_items_per_xcd, (cus / 8) * occ));
   hipLaunchKernelGGL((gemm_mfma_kernel<WF, BMT, EPI, TC, WQ, GROUPED>), dim3(8 * wg_per_xcd),
                      dim3(256), 0, s, a, nft, slots, wg_per_xcd);

@@ -46,8 +46,12 @@ hipError_t launch_norm_gate(int act_dt, const void* hidden, const void* gamma, c
                             float eps, hipStream_t s);
 hipError_t launch_topk(const float* logits, int n, int E, int k, float scale, int* ids, float* w,
                        hipStream_t s);
+// Stable route sort. With a `bcnt` scratch of route_sort_blocks(R) * E ints
+// and R above one block's chunk, two multi-block launches; else one workgroup.
 hipError_t launch_route_sort(const int* ids, int R, int E, int* counts, int* offsets, int* perm,
-                             int* inv, int bm, int2* tiles, int* num_tiles, hipStream_t s);
+                             int* inv, int bm, int2* tiles, int* num_tiles, int* bcnt,
+                             hipStream_t s);
+int route_sort_blocks(int R);
 
 // fp32 SIMT GEMM (64x64 tiles, bm must be 64 in grouped mode); C fp32.
 hipError_t launch_gemm_simt_f32(const GemmArgs& a, int epi, int grid_y, hipStream_t s);

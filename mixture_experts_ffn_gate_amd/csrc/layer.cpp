@@ -85,6 +85,7 @@ struct moe_layer {
   int* inv = nullptr;
   int2* tiles = nullptr;
   int* num_tiles = nullptr;
+  int* bcnt = nullptr;    // per-block expert counts of the multi-block sort
   void* g_sh = nullptr;   // shared-expert activation [N][S]
   void* sh = nullptr;     // shared-expert output [N][H]
   void* z = nullptr;      // latent input [N][L]
@@ -344,6 +345,7 @@ int moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_weights_t* w
   TRY(dalloc(L, (void**)&L->inv, R * 4));
   TRY(dalloc(L, (void**)&L->tiles, tiles_cap * sizeof(int2)));
   TRY(dalloc(L, (void**)&L->num_tiles, 16));
+  TRY(dalloc(L, (void**)&L->bcnt, (size_t)route_sort_blocks((int)R) * E * 4));
   if (S > 0) {
     TRY(dalloc(L, &L->g_sh, (size_t)N * S * as));
     TRY(dalloc(L, &L->sh, (size_t)N * H * as));
@@ -442,7 +444,7 @@ int moe_layer_forward(moe_layer_t* L, void* hidden, void* residual, int32_t n, v
   {
     StageScope sc(L, MOE_STAGE_SORT, s);
     HIP_TRY(launch_route_sort(L->ids, R, E, L->counts, L->offsets, L->perm, L->inv, bm,
-                              L->tiles, L->num_tiles, s));
+                              L->tiles, L->num_tiles, L->bcnt, s));
   }
   const int tiles_cap = (R + bm - 1) / bm + std::min(E, R);
 
@@ -548,7 +550,8 @@ int moe_layer_debug_read(moe_layer_t* L, int32_t which, void* dst, int64_t bytes
     case MOE_DBG_INV: src = L->inv; avail = R * 4; break;
     default: return fail(MOE_ERR_INVALID_ARG, "unknown debug buffer %d", which);
   }
-  if (n == 0 || bytes > avail)
+  if (n == 0) return fail(MOE_ERR_INVALID_ARG, "debug_read before any forward of this layer");
+  if (bytes > avail)
     return fail(MOE_ERR_INVALID_ARG, "debug_read of %lld bytes exceeds the %lld written",
                 (long long)bytes, (long long)avail);
   HIP_TRY(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, (hipStream_t)stream));
@@ -573,7 +576,7 @@ int moe_route_sort(const int32_t* ids, int32_t n, int32_t k, int32_t E, int32_t*
   if (E < 1 || E > MOE_MAX_EXPERTS)
     return fail(MOE_ERR_INVALID_CONFIG, "E=%d outside 1..%d", E, MOE_MAX_EXPERTS);
   HIP_TRY(launch_route_sort(ids, n * k, E, counts, offsets, perm, inv, 0, nullptr, nullptr,
-                            (hipStream_t)stream));
+                            nullptr, (hipStream_t)stream));
   return MOE_OK;
 }
 

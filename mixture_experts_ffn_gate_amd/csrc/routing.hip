@@ -416,6 +416,134 @@ __global__ void __launch_bounds__(1024) route_sort_kernel(const int* __restrict_
 }
 
 // ---------------------------------------------------------------------------
+// Multi-block stable route sort for large R (two launches).
+//   route_hist_kernel: block b counts the experts of routes [b*CH, (b+1)*CH)
+//                      -> bcnt[b][E]
+//   route_scatter_kernel: block b adds up bcnt over all blocks (totals and the
+//                      part of lower blocks), scans over experts, and scatters
+//                      its own chunk in order with the same ballot ranking as
+//                      route_sort_kernel. Block 0 also writes counts, offsets
+//                      and the tile list. Same result as the one-block kernel.
+// ---------------------------------------------------------------------------
+constexpr int SORT_CH = 2048;  // routes per block (2 per thread)
+
+__global__ void __launch_bounds__(1024) route_hist_kernel(const int* __restrict__ ids, int R, int E,
+                                                          int* __restrict__ bcnt) {
+  __shared__ int cnt[MOE_MAX_E];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < MOE_MAX_E; e += 1024) cnt[e] = 0;
+  __syncthreads();
+  const int r0 = blockIdx.x * SORT_CH;
+  int ev[SORT_CH / 1024];
+#pragma unroll
+  for (int i = 0; i < SORT_CH / 1024; ++i) {
+    const int r = r0 + i * 1024 + tid;
+    ev[i] = r < R ? ids[r] : -1;
+  }
+#pragma unroll
+  for (int i = 0; i < SORT_CH / 1024; ++i)
+    if (ev[i] >= 0 && ev[i] < E) atomicAdd(&cnt[ev[i]], 1);
+  __syncthreads();
+  for (int e = tid; e < E; e += 1024) bcnt[(size_t)blockIdx.x * E + e] = cnt[e];
+}
+
+__global__ void __launch_bounds__(1024) route_scatter_kernel(
+    const int* __restrict__ ids, int R, int E, const int* __restrict__ bcnt,
+    int* __restrict__ counts, int* __restrict__ offsets, int* __restrict__ perm,
+    int* __restrict__ inv, int bm, int2* __restrict__ tiles, int* __restrict__ num_tiles) {
+  __shared__ int base[MOE_MAX_E];
+  __shared__ int wcnt[16][MOE_MAX_E];
+  __shared__ int wsum[2][16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nb = gridDim.x, b = blockIdx.x;
+  for (int e = tid; e < MOE_MAX_E; e += 1024)
+#pragma unroll
+    for (int w = 0; w < 16; ++w) wcnt[w][e] = 0;
+  // Totals and lower-block parts per expert (E <= 512 < 1024 threads).
+  int c = 0, lower = 0;
+  if (tid < E) {
+    for (int bb = 0; bb < nb; ++bb) {
+      const int v = bcnt[(size_t)bb * E + tid];
+      c += v;
+      if (bb < b) lower += v;
+    }
+  }
+  const int tc = (tid < E && bm > 0) ? (c + bm - 1) / bm : 0;
+  const int ic = wave_incl_scan(c, lane), itc = wave_incl_scan(tc, lane);
+  if (lane == 63) {
+    wsum[0][wave] = ic;
+    wsum[1][wave] = itc;
+  }
+  __syncthreads();
+  int pc = 0, ptc = 0;
+  for (int w = 0; w < wave; ++w) {
+    pc += wsum[0][w];
+    ptc += wsum[1][w];
+  }
+  if (tid < E) {
+    const int excl = pc + ic - c;
+    base[tid] = excl + lower;
+    if (b == 0) {
+      const int texcl = ptc + itc - tc;
+      counts[tid] = c;
+      offsets[tid] = excl;
+      if (tid == E - 1) {
+        offsets[E] = excl + c;
+        if (num_tiles) *num_tiles = texcl + tc;
+      }
+      if (tiles)
+        for (int i = 0; i < tc; ++i) tiles[texcl + i] = make_int2(tid, i * bm);
+    }
+  }
+  __syncthreads();
+
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int r0 = b * SORT_CH;
+  int ev[SORT_CH / 1024];
+#pragma unroll
+  for (int i = 0; i < SORT_CH / 1024; ++i) {
+    const int r = r0 + i * 1024 + tid;
+    ev[i] = r < R ? ids[r] : -1;
+  }
+#pragma unroll
+  for (int i = 0; i < SORT_CH / 1024; ++i) {
+    const int c0 = r0 + i * 1024;
+    if (c0 >= R) break;  // uniform across the block
+    const int r = c0 + tid;
+    const bool valid = ev[i] >= 0 && ev[i] < E;
+    const int e = valid ? ev[i] : -1;
+    uint64_t mask = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 10; ++bit) {
+      const bool on = valid && ((e >> bit) & 1);
+      const uint64_t bal = __ballot(on);
+      mask &= on ? bal : ~bal;
+    }
+    const int rank = __popcll(mask & below);
+    if (valid && rank == 0) wcnt[wave][e] = __popcll(mask);
+    __syncthreads();
+    if (valid) {
+      int pre = 0;
+      for (int w = 0; w < wave; ++w) pre += wcnt[w][e];
+      const int pos = base[e] + pre + rank;
+      perm[pos] = r;
+      inv[r] = pos;
+    }
+    __syncthreads();
+    for (int ee = tid; ee < E; ee += 1024) {
+      int sum = 0;
+#pragma unroll
+      for (int w = 0; w < 16; ++w) {
+        sum += wcnt[w][ee];
+        wcnt[w][ee] = 0;
+      }
+      base[ee] += sum;
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 template <int TM>
@@ -494,8 +622,20 @@ hipError_t launch_topk(const float* logits, int n, int E, int k, float scale, in
 }
 
 hipError_t launch_route_sort(const int* ids, int R, int E, int* counts, int* offsets, int* perm,
-                             int* inv, int bm, int2* tiles, int* num_tiles, hipStream_t s) {
-  hipLaunchKernelGGL(route_sort_kernel, dim3(1), dim3(1024), 0, s, ids, R, E, counts, offsets,
-                     perm, inv, bm, tiles, num_tiles);
+                             int* inv, int bm, int2* tiles, int* num_tiles, int* bcnt,
+                             hipStream_t s) {
+  const int nb = (R + SORT_CH - 1) / SORT_CH;
+  if (bcnt == nullptr || nb <= 1) {
+    hipLaunchKernelGGL(route_sort_kernel, dim3(1), dim3(1024), 0, s, ids, R, E, counts, offsets,
+                       perm, inv, bm, tiles, num_tiles);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(route_hist_kernel, dim3(nb), dim3(1024), 0, s, ids, R, E, bcnt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(route_scatter_kernel, dim3(nb), dim3(1024), 0, s, ids, R, E, bcnt, counts,
+                     offsets, perm, inv, bm, tiles, num_tiles);
   return hipGetLastError();
 }
+
+int route_sort_blocks(int R) { return (R + SORT_CH - 1) / SORT_CH; }

@@ -1,0 +1,131 @@
+"""rocprofv3 output -> short text summaries and the measured HBM traffic record.
+
+    python -m mixture_experts_ffn_gate_amd.profiling stats  STATS_CSV  OUT_MD  --cmd "..."
+    python -m mixture_experts_ffn_gate_amd.profiling traffic FETCH_CSV WRITE_CSV OUT_JSON \
+        --calib-mib 512 --workload NAME --cmd "..."
+
+``traffic`` reads two ``--pmc`` runs (FETCH_SIZE, then WRITE_SIZE; KiB per
+dispatch) of a ``bench.py --calibrate-copy-mib M`` command. The M MiB
+device-to-device copy in the same run gives each counter's scale factor:
+true KiB / counted KiB. The record stores, per layer kernel, the mean scaled
+bytes per dispatch, plus a hash of the GEMM source. ``bench.py`` reports the
+traffic only while that hash matches the current source.
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import re
+from collections import defaultdict
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ("csrc/gemm.hip", "csrc/routing.hip", "csrc/reduce.hip")
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(HERE, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+_MANGLED = re.compile(r"gemm_mfma_kernelILi(\d+)ELi(\d+)ELi(\d+)E(\w+?)Li(\d+)ELb(\d)E")
+_DEMANGLED = re.compile(r"gemm_mfma_kernel<(\d+), (\d+), (\d+), ([\w ]+), (\d+), (true|false)>")
+_EPI = {"0": "relu2", "1": "store", "2": "add_res"}
+
+
+def short_name(name: str) -> str:
+    """Readable kernel label; GEMMs by role (grouped/dense, epilogue, weights, tile)."""
+    m = _MANGLED.search(name) or _DEMANGLED.search(name)
+    if m:
+        wf, bmt, epi, _, wq, g = m.groups()
+        grouped = g in ("1", "true")
+        return (f"gemm[{'grouped' if grouped else 'dense'},{_EPI.get(epi, epi)},"
+                f"{'nvfp4' if wq == '1' else 'bf16'},{int(wf) * 4}x{bmt}]")
+    for key in ("norm_gate", "topk_sigmoid", "route_sort", "unpermute_reduce", "retile",
+                "nvfp4_pack", "nvfp4_scale2", "copyBuffer"):
+        if key in name:
+            return key
+    if "at::native" in name:
+        return "torch:" + name.split("at::native::")[1].split("<")[0][:40]
+    return name[:60]
+
+
+def stats(csv_path: str, out_md: str, cmd: str) -> None:
+    rows = list(csv.DictReader(open(csv_path)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = [f"# Kernel durations: `{os.path.basename(out_md)}`", "",
+             "Command:", "", "```", cmd, "```", "",
+             "| kernel | symbol (truncated) | calls | avg µs | min µs | max µs |",
+             "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {short_name(r['Name'])} | `{r['Name'][:70]}` | {r['Calls']} | "
+                     f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                     f"{float(r['MaxNs']) / 1e3:.1f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def _per_dispatch(csv_path: str, counter: str):
+    out = []
+    for r in csv.DictReader(open(csv_path)):
+        if r["Counter_Name"] == counter:
+            out.append((r["Kernel_Name"], int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+    return out
+
+
+def traffic(fetch_csv: str, write_csv: str, out_json: str, calib_mib: int, workload: str,
+            cmd: str) -> None:
+    calib_kib = calib_mib * 1024
+    rec = {"workload": workload, "source_hash": source_hash(), "command": cmd,
+           "calibration_copy_kib": calib_kib, "kernels": {}}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _per_dispatch(path, counter)
+        # The calibration copy: the runtime's device-to-device copy kernel with
+        # the largest count (the known-size copy; the layer's own copies are
+        # a few KiB).
+        copies = [v for n, _, v in rows if "copyBuffer" in n]
+        counted = max(copies) if copies else 0.0
+        factor = calib_kib / counted if counted > 0 else None
+        rec[f"{counter.lower()}_factor"] = factor
+        acc = defaultdict(list)
+        for name, _, v in rows:
+            acc[short_name(name)].append(v)
+        for k, vals in acc.items():
+            if factor is None:
+                continue
+            d = rec["kernels"].setdefault(k, {})
+            d[f"{counter.lower()}_bytes"] = sum(vals) / len(vals) * factor * 1024
+            d["dispatches"] = len(vals)
+    with open(out_json, "w") as f:
+        json.dump(rec, f, indent=1)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd_name", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("out")
+    s.add_argument("--cmd", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch_csv")
+    t.add_argument("write_csv")
+    t.add_argument("out")
+    t.add_argument("--calib-mib", type=int, required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--cmd", required=True)
+    a = ap.parse_args()
+    if a.cmd_name == "stats":
+        stats(a.csv, a.out, a.cmd)
+    else:
+        traffic(a.fetch_csv, a.write_csv, a.out, a.calib_mib, a.workload, a.cmd)
+
+
+if __name__ == "__main__":
+    main()

@@ -172,8 +172,13 @@ def test_skewed_routing_many_row_blocks(ml):
     pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"])
 
 
-def test_sort_stage_bit_exact_inside_forward(ml):
-    wl = SMALL["direct_ragged"]
+@pytest.mark.parametrize("name", ["direct_ragged", "multiblock_sort", "multiblock_512"])
+def test_sort_stage_bit_exact_inside_forward(ml, name):
+    # Large route counts take the multi-block sort (2048 routes per block).
+    wl = {"direct_ragged": SMALL["direct_ragged"],
+          "multiblock_sort": wlm.Workload("mb", H=256, E=32, k=8, I=64, S=0, L=0, N=1000),
+          "multiblock_512": wlm.Workload("mb512", H=256, E=512, k=16, I=64, S=0, L=0, N=301),
+          }[name]
     r = run_layer(ml, wl, wl.N, seed=2)
     L = r["layer"]
     R = wl.N * wl.k
