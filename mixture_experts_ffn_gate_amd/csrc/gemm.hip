@@ -483,6 +483,132 @@ hipError_t launch_gemm_mfma(const GemmArgs& a, MfmaCfg cfg, int epi, bool tc_bf1
 }
 
 // ---------------------------------------------------------------------------
+// Decode-sized GEMV arm (at most 16 rows per row tile).
+// One launch covers up to two segments: the routed experts (grouped, tile
+// list) and the shared expert (dense), so small batches need no side stream.
+// Item = (segment, row tile, 16-feature tile); one workgroup per item; the 4
+// waves split the k-steps of the item and each issues the loads of GU steps
+// at a time (weights and the <= 16 activation rows straight from memory into
+// MFMA registers), so many loads are in flight per CU even for one token.
+// The partial sums meet in LDS and are added in wave order (deterministic).
+// ---------------------------------------------------------------------------
+#ifndef MOE_GEMV_GU
+#define MOE_GEMV_GU 4
+#endif
+struct GemvArgs {
+  GemmArgs seg[2];
+  int nseg;
+  int nft[2];    // 16-feature tiles per segment
+  int slots[2];  // row-tile slots per segment (grouped: tile-list capacity)
+};
+
+template <int EPI, typename TC, int WQ>
+__global__ void __launch_bounds__(256) gemv_kernel(GemvArgs g) {
+  constexpr int GU = MOE_GEMV_GU;  // k-steps per load group
+  using Src = WSrc<WQ, 1>;
+  using Frag = typename Src::Frag;
+  __shared__ floatx4 part[3][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // Segment 1 (dense, every item live, the longer K at these shapes) takes
+  // the first block indices so that its items start first.
+  int item = blockIdx.x;
+  int sg = 0;
+  if (g.nseg > 1) {
+    const int n1 = g.slots[1] * g.nft[1];
+    if (item < n1) sg = 1;
+    else item -= n1;
+  }
+  const GemmArgs& a = g.seg[sg];
+  const int slot = item / g.nft[sg];
+  const int ftile = item - slot * g.nft[sg];
+  TileInfo ti;
+  if (!decode_tile(a, slot, 16, ti)) return;  // uniform: the whole workgroup leaves
+
+  const int nsteps = a.K / 64;
+  const int s0 = wave * nsteps / 4, s1 = (wave + 1) * nsteps / 4;
+  const int nf0 = ftile * 16;
+  Src src;
+  src.init(a, ti.g, nf0, lane);
+  const int r = min(lane & 15, ti.rows - 1);
+  const bf16* xp = (const bf16*)a.A + (size_t)a_row_of(a, ti.row0 + r) * a.lda + (lane >> 4) * 8;
+
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int kb = s0; kb < s1; kb += GU) {
+    Frag w[GU];
+    bf16x8 x[GU][2];
+#pragma unroll
+    for (int u = 0; u < GU; ++u) {
+      const int ks = min(kb + u, s1 - 1);  // past the range: a valid step, not used
+      src.load(w[u], ks);
+      x[u][0] = *(const bf16x8*)(xp + ks * 64);
+      x[u][1] = *(const bf16x8*)(xp + ks * 64 + 32);
+    }
+#pragma unroll
+    for (int u = 0; u < GU; ++u) {
+      if (kb + u >= s1) break;
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(src.get(w[u], 0, s, lane), x[u][s], acc, 0,
+                                                      0, 0);
+    }
+  }
+  if (wave > 0) part[wave - 1][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  acc += part[0][lane];
+  acc += part[1][lane];
+  acc += part[2][lane];
+  const int n = nf0 + 4 * (lane >> 4);
+  const int row = lane & 15;
+  const int p = ti.row0 + row;
+  if (n < a.N && row < ti.rows) {
+    if (WQ == 1) acc *= a.b_scale2[ti.g];
+    if (EPI == EPI_RELU2) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = relu2(acc[q]);
+    }
+    if (EPI == EPI_ADD_RES) {
+      acc += store4<TC>::ld((const TC*)a.res + (size_t)p * a.ldc + n);
+      if (a.add) acc += store4<TC>::ld((const TC*)a.add + (size_t)p * a.ldc + n);
+    }
+    store4<TC>::st((TC*)a.C + (size_t)p * a.ldc + n, acc);
+  }
+}
+
+hipError_t launch_gemv(const GemmArgs* segs, const int* slots, int nseg, int epi, bool nvfp4,
+                       hipStream_t s) {
+  GemvArgs g{};
+  g.nseg = nseg;
+  int total = 0;
+  for (int i = 0; i < nseg; ++i) {
+    g.seg[i] = segs[i];
+    g.nft[i] = (segs[i].N + 15) / 16;
+    g.slots[i] = slots[i];
+    total += g.nft[i] * slots[i];
+  }
+  if (total == 0) return hipSuccess;
+  dim3 grid(total);
+#define GEMV_LAUNCH(E, Q)                                                                      \
+  hipLaunchKernelGGL((gemv_kernel<E, bf16, Q>), grid, dim3(256), 0, s, g)
+  if (nvfp4) {
+    switch (epi) {
+      case EPI_RELU2: GEMV_LAUNCH(EPI_RELU2, 1); break;
+      case EPI_STORE: GEMV_LAUNCH(EPI_STORE, 1); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (epi) {
+      case EPI_RELU2: GEMV_LAUNCH(EPI_RELU2, 0); break;
+      case EPI_STORE: GEMV_LAUNCH(EPI_STORE, 0); break;
+      case EPI_ADD_RES: GEMV_LAUNCH(EPI_ADD_RES, 0); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+#undef GEMV_LAUNCH
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Re-tile [G][N][K] row-major bf16 into [G][N/16][K/32][64][8] (MFMA A-operand
 // lane order). One thread per 16-byte destination chunk.
 // ---------------------------------------------------------------------------

@@ -53,6 +53,15 @@ hipError_t launch_route_sort(const int* ids, int R, int E, int* counts, int* off
                              hipStream_t s);
 int route_sort_blocks(int R);
 
+// Decode-sized routing in one launch (bf16, n <= 16): norm + residual + gate,
+// then (last block) top-k and the stable sort. `done` is a zeroed device
+// counter that the kernel leaves at zero.
+hipError_t launch_route_small(const void* hidden, const void* gamma, const void* wgate,
+                              void* normed, void* residual, float* logits, int n, int H, int E,
+                              float eps, int k, float scale, int* ids, float* w, int* counts,
+                              int* offsets, int* perm, int* inv, int bm, int2* tiles,
+                              int* num_tiles, unsigned* done, hipStream_t s);
+
 // fp32 SIMT GEMM (64x64 tiles, bm must be 64 in grouped mode); C fp32.
 hipError_t launch_gemm_simt_f32(const GemmArgs& a, int epi, int grid_y, hipStream_t s);
 
@@ -65,6 +74,12 @@ struct MfmaCfg {
 // `slots` = row tiles (grouped: tile-list capacity, live count read on device).
 hipError_t launch_gemm_mfma(const GemmArgs& a, MfmaCfg cfg, int epi, bool tc_bf16, bool nvfp4,
                             int slots, hipStream_t s);
+
+// Decode-sized GEMV arm (row tiles of <= 16 rows, bf16 activations and
+// output): nseg (1 or 2) segments in one launch, each with `slots` row tiles;
+// grouped segments set `tiles`.
+hipError_t launch_gemv(const GemmArgs* segs, const int* slots, int nseg, int epi, bool nvfp4,
+                       hipStream_t s);
 
 // Re-tile bf16 [G][N][K] row-major weights into the MFMA lane order.
 hipError_t launch_retile_bf16(const bf16* src, bf16* dst, int G, int N, int K, hipStream_t s);

@@ -56,6 +56,9 @@ size_t dt_size(int dt) { return dt == MOE_DT_F32 ? 4 : 2; }
 
 }  // namespace
 
+// Counter of the decode-sized routing kernel.
+constexpr size_t kSyncWords = 1;
+
 struct moe_layer {
   moe_layer_config_t cfg{};
   int device = 0;
@@ -86,6 +89,7 @@ struct moe_layer {
   int2* tiles = nullptr;
   int* num_tiles = nullptr;
   int* bcnt = nullptr;    // per-block expert counts of the multi-block sort
+  unsigned* sync = nullptr;  // zeroed counter of the decode-sized routing (left at zero)
   void* g_sh = nullptr;   // shared-expert activation [N][S]
   void* sh = nullptr;     // shared-expert output [N][H]
   void* z = nullptr;      // latent input [N][L]
@@ -255,6 +259,87 @@ void set_weights(const moe_layer* L, GemmArgs& a, const void* w, const void* sc,
   }
 }
 
+// Decode-sized arm (bf16/NVFP4 layers, N <= MOE_GEMV_MAX_N): one stream; the
+// shared expert rides as a second segment of the grouped GEMV launches.
+constexpr int MOE_GEMV_MAX_N = 16;
+
+int forward_small(moe_layer* L, void* hidden, void* residual, int n, hipStream_t s) {
+  const moe_layer_config_t& c = L->cfg;
+  const int H = c.hidden_size, E = c.num_experts, k = c.top_k, I = c.moe_inter,
+            S = c.shared_inter, Lt = c.latent_size, D = L->D();
+  const int R = n * k;
+  const int dslots = (n + 15) / 16;
+  const int bm = 16;
+  {
+    // norm + gate + top-k + sort in one launch (timed as the norm_gate stage)
+    StageScope sc(L, MOE_STAGE_NORM_GATE, s);
+    HIP_TRY(launch_route_small(hidden, L->gamma, L->gate, L->normed, residual, L->logits, n, H,
+                               E, c.rms_eps, k, c.routed_scaling_factor, L->ids, L->w,
+                               L->counts, L->offsets, L->perm, L->inv, bm, L->tiles,
+                               L->num_tiles, L->sync, s));
+  }
+  const void* zin = L->normed;
+  if (Lt > 0) {
+    StageScope sc(L, MOE_STAGE_FC1, s);
+    GemmArgs a{};
+    a.A = L->normed; a.lda = H; a.B = L->fc1; a.C = L->z; a.ldc = Lt;
+    a.M = n; a.N = Lt; a.K = H;
+    HIP_TRY(launch_gemv(&a, &dslots, 1, EPI_STORE, false, s));
+    zin = L->z;
+  }
+  const int tiles_cap = (R + bm - 1) / bm + std::min(E, R);
+  const int slots[2] = {tiles_cap, dslots};
+  const int nseg = S > 0 ? 2 : 1;
+  {
+    StageScope sc(L, MOE_STAGE_GROUPED_UP, s);
+    GemmArgs g[2] = {};
+    g[0].A = zin; g[0].lda = D; g[0].a_rows = L->perm; g[0].a_div = k;
+    set_weights(L, g[0], L->up, L->up_s, L->up_s2, I, D);
+    g[0].C = L->h; g[0].ldc = I; g[0].N = I; g[0].K = D;
+    g[0].tiles = L->tiles; g[0].num_tiles = L->num_tiles; g[0].offsets = L->offsets; g[0].bm = bm;
+    if (S > 0) {
+      g[1].A = L->normed; g[1].lda = H; g[1].C = L->g_sh; g[1].ldc = S;
+      g[1].M = n; g[1].N = S; g[1].K = H;
+      set_weights(L, g[1], L->sh_up, L->sh_up_s, L->sh_up_s2, S, H);
+    }
+    HIP_TRY(launch_gemv(g, slots, nseg, EPI_RELU2, L->nvfp4, s));
+  }
+  {
+    StageScope sc(L, MOE_STAGE_GROUPED_DOWN, s);
+    GemmArgs g[2] = {};
+    g[0].A = L->h; g[0].lda = I;
+    set_weights(L, g[0], L->down, L->down_s, L->down_s2, D, I);
+    g[0].C = L->y; g[0].ldc = D; g[0].N = D; g[0].K = I;
+    g[0].tiles = L->tiles; g[0].num_tiles = L->num_tiles; g[0].offsets = L->offsets; g[0].bm = bm;
+    if (S > 0) {
+      g[1].A = L->g_sh; g[1].lda = S; g[1].C = L->sh; g[1].ldc = H;
+      g[1].M = n; g[1].N = H; g[1].K = S;
+      set_weights(L, g[1], L->sh_down, L->sh_down_s, L->sh_down_s2, H, S);
+    }
+    HIP_TRY(launch_gemv(g, slots, nseg, EPI_STORE, L->nvfp4, s));
+  }
+  if (Lt == 0) {
+    StageScope sc(L, MOE_STAGE_REDUCE, s);
+    HIP_TRY(launch_unpermute_reduce(c.act_dtype, false, L->y, L->inv, L->w, n, k, D, residual,
+                                    S > 0 ? L->sh : nullptr, hidden, s));
+  } else {
+    {
+      StageScope sc(L, MOE_STAGE_REDUCE, s);
+      HIP_TRY(launch_unpermute_reduce(c.act_dtype, true, L->y, L->inv, L->w, n, k, D, nullptr,
+                                      nullptr, L->o, s));
+    }
+    StageScope sc(L, MOE_STAGE_FC2, s);
+    GemmArgs a{};
+    a.A = L->o; a.lda = Lt; a.B = L->fc2; a.C = hidden; a.ldc = H;
+    a.M = n; a.N = H; a.K = Lt;
+    a.res = residual; a.add = S > 0 ? L->sh : nullptr;
+    HIP_TRY(launch_gemv(&a, &dslots, 1, EPI_ADD_RES, false, s));
+  }
+  L->last_n = n;
+  if (L->timing && L->timing_count < L->timing_cap) L->timing_count++;
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -346,6 +431,8 @@ int moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_weights_t* w
   TRY(dalloc(L, (void**)&L->tiles, tiles_cap * sizeof(int2)));
   TRY(dalloc(L, (void**)&L->num_tiles, 16));
   TRY(dalloc(L, (void**)&L->bcnt, (size_t)route_sort_blocks((int)R) * E * 4));
+  TRY(dalloc(L, (void**)&L->sync, kSyncWords * 4));
+  TRYH(hipMemsetAsync(L->sync, 0, kSyncWords * 4, s));
   if (S > 0) {
     TRY(dalloc(L, &L->g_sh, (size_t)N * S * as));
     TRY(dalloc(L, &L->sh, (size_t)N * H * as));
@@ -382,6 +469,7 @@ int moe_layer_forward(moe_layer_t* L, void* hidden, void* residual, int32_t n, v
     return fail(MOE_ERR_TOO_MANY_TOKENS, "num_tokens=%d > max_tokens=%d", n, c.max_tokens);
   if (n == 0) return MOE_OK;
   hipStream_t s = (hipStream_t)stream;
+  if (L->mfma && n <= MOE_GEMV_MAX_N) return forward_small(L, hidden, residual, n, s);
   const int H = c.hidden_size, E = c.num_experts, k = c.top_k, I = c.moe_inter,
             S = c.shared_inter, Lt = c.latent_size, D = L->D();
   const int R = n * k;

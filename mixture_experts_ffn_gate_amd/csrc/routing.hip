@@ -241,20 +241,16 @@ __global__ void __launch_bounds__(256) norm_gate_mfma_kernel(const bf16* __restr
 // 64-bit max reduction pick the experts in slot order (score desc, index asc).
 // ---------------------------------------------------------------------------
 template <int EPL>
-__global__ void __launch_bounds__(256) topk_sigmoid_kernel(const float* __restrict__ logits,
-                                                           int n, int E, int k, float scale,
-                                                           int* __restrict__ ids,
-                                                           float* __restrict__ wout) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= n) return;
+__device__ __forceinline__ void topk_token(const float* __restrict__ lrow, int E, int k,
+                                           float scale, int* __restrict__ ids_row,
+                                           float* __restrict__ w_row, int lane) {
   uint64_t key[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     int e = lane + 64 * i;
     key[i] = 0;
     if (e < E) {
-      float l = logits[(size_t)t * E + e];
+      float l = lrow[e];
       float s = 1.0f / (1.0f + expf(-l));
       key[i] = ((uint64_t)__float_as_uint(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
     }
@@ -276,9 +272,21 @@ __global__ void __launch_bounds__(256) topk_sigmoid_kernel(const float* __restri
   }
   if (lane < k) {
     float wv = sum > 0.f ? my_s / sum : 1.0f / (float)k;
-    ids[(size_t)t * k + lane] = my_e;
-    wout[(size_t)t * k + lane] = wv * scale;
+    ids_row[lane] = my_e;
+    w_row[lane] = wv * scale;
   }
+}
+
+template <int EPL>
+__global__ void __launch_bounds__(256) topk_sigmoid_kernel(const float* __restrict__ logits,
+                                                           int n, int E, int k, float scale,
+                                                           int* __restrict__ ids,
+                                                           float* __restrict__ wout) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= n) return;
+  topk_token<EPL>(logits + (size_t)t * E, E, k, scale, ids + (size_t)t * k, wout + (size_t)t * k,
+                  lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -303,18 +311,23 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v;
 }
 
-__global__ void __launch_bounds__(1024) route_sort_kernel(const int* __restrict__ ids, int R,
-                                                          int E, int* __restrict__ counts,
-                                                          int* __restrict__ offsets,
-                                                          int* __restrict__ perm,
-                                                          int* __restrict__ inv, int bm,
-                                                          int2* __restrict__ tiles,
-                                                          int* __restrict__ num_tiles) {
+struct SortLds {
+  int cnt[MOE_MAX_E];
+  int base[MOE_MAX_E];
+  int wcnt[16][MOE_MAX_E];
+  int wsum[2][16];
+};
+
+// The whole one-workgroup sort (1024 threads; every thread must call it).
+__device__ void sort_block(const int* __restrict__ ids, int R, int E, int* __restrict__ counts,
+                           int* __restrict__ offsets, int* __restrict__ perm,
+                           int* __restrict__ inv, int bm, int2* __restrict__ tiles,
+                           int* __restrict__ num_tiles, SortLds& L) {
   constexpr int RPT = 16;  // routes per thread loaded per batch (one load latency)
-  __shared__ int cnt[MOE_MAX_E];
-  __shared__ int base[MOE_MAX_E];
-  __shared__ int wcnt[16][MOE_MAX_E];
-  __shared__ int wsum[2][16];
+  int* cnt = L.cnt;
+  int* base = L.base;
+  auto& wcnt = L.wcnt;
+  auto& wsum = L.wsum;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   for (int e = tid; e < MOE_MAX_E; e += 1024) {
@@ -413,6 +426,17 @@ __global__ void __launch_bounds__(1024) route_sort_kernel(const int* __restrict_
       __syncthreads();
     }
   }
+}
+
+__global__ void __launch_bounds__(1024) route_sort_kernel(const int* __restrict__ ids, int R,
+                                                          int E, int* __restrict__ counts,
+                                                          int* __restrict__ offsets,
+                                                          int* __restrict__ perm,
+                                                          int* __restrict__ inv, int bm,
+                                                          int2* __restrict__ tiles,
+                                                          int* __restrict__ num_tiles) {
+  __shared__ SortLds lds;
+  sort_block(ids, R, E, counts, offsets, perm, inv, bm, tiles, num_tiles, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -544,6 +568,126 @@ __global__ void __launch_bounds__(1024) route_scatter_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Decode-sized routing front end in one launch (N <= 16 tokens, bf16).
+// Block b (16 waves) computes RMSNorm and the gate logits of experts
+// [16b, 16b+16) for all tokens, the k-steps dealt over its 16 waves (same hi+lo
+// fp32 split as the batched kernel) and summed in wave order; block 0 writes
+// normed and residual. The last block to finish (device-scope release fence,
+// then a global counter; acquire fence after) runs the top-k of every token
+// (one wave each) and the one-block stable sort, then re-arms the counter.
+// Device-scope fences write back / invalidate the L2 of the issuing XCD, so
+// each block issues as few as the data flow needs (one wave).
+// ---------------------------------------------------------------------------
+template <int EPL>
+__global__ void __launch_bounds__(1024) route_small_kernel(
+    const bf16* __restrict__ hidden, const bf16* __restrict__ gamma, const bf16* __restrict__ wgate,
+    bf16* __restrict__ normed, bf16* __restrict__ residual, float* __restrict__ logits, int n,
+    int H, int E, float eps, int k, float scale, int* __restrict__ ids, float* __restrict__ wts,
+    int* __restrict__ counts, int* __restrict__ offsets, int* __restrict__ perm,
+    int* __restrict__ inv, int bm, int2* __restrict__ tiles, int* __restrict__ num_tiles,
+    unsigned* __restrict__ done) {
+  __shared__ float rinv[16];
+  __shared__ floatx4 red[16][64];
+  __shared__ SortLds slds;
+  __shared__ int is_last;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int e0 = blockIdx.x * 16;
+
+  // 1. inverse RMS: wave t takes token t
+  {
+    float ss = 0.f;
+    if (wave < n) {
+      const bf16* x = hidden + (size_t)wave * H;
+      for (int i0 = lane * 8; i0 < H; i0 += 512 * 4) {
+        bf16x8 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = i0 + u * 512 < H ? *(const bf16x8*)(x + i0 + u * 512) : bf16x8{};
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const float f = (float)v[u][q];
+            ss += f * f;
+          }
+      }
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) rinv[wave] = 1.0f / sqrtf(ss / (float)H + eps);
+  }
+  __syncthreads();
+
+  // 2. gate logits of this block's 16 experts; wave w takes k-steps w, w+16, ...
+  const int tok = lane & 15, kg = lane >> 4;
+  const bool tvalid = tok < n;
+  const float rv = rinv[tok];
+  const bool writer = blockIdx.x == 0;
+  const bf16* wrow = wgate + (size_t)min(e0 + tok, E - 1) * H + kg * 8;
+  const size_t row = (size_t)tok * H + kg * 8;
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  constexpr int U = 8;
+  for (int kb = wave * 32; kb < H; kb += 512 * U) {
+    bf16x8 wf[U], xv[U], gv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k0 = min(kb + u * 512, H - 32);  // past the end: a valid step, not used
+      wf[u] = *(const bf16x8*)(wrow + k0);
+      xv[u] = tvalid ? *(const bf16x8*)(hidden + row + k0) : bf16x8{};
+      gv[u] = *(const bf16x8*)(gamma + k0 + kg * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k0 = kb + u * 512;
+      if (k0 >= H) break;
+      bf16x8 hi, lo, nb;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float v = (float)xv[u][q] * rv * (float)gv[u][q];
+        hi[q] = (bf16)v;
+        lo[q] = (bf16)(v - (float)hi[q]);
+        nb[q] = hi[q];
+      }
+      if (writer && tvalid) {
+        *(bf16x8*)(residual + row + k0) = xv[u];
+        *(bf16x8*)(normed + row + k0) = nb;
+      }
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u], hi, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u], lo, acc, 0, 0, 0);
+    }
+  }
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    floatx4 v = red[0][lane];
+#pragma unroll
+    for (int w = 1; w < 16; ++w) v += red[w][lane];
+    const int e = e0 + 4 * kg;
+    if (tvalid)
+      for (int q = 0; q < 4; ++q)
+        if (e + q < E) logits[(size_t)tok * E + e + q] = v[q];
+  }
+
+  // 3. the last block finishes routing. Only wave 0 stored logits, so only it
+  // fences (release before the count; acquire after it, in the last block,
+  // ahead of the barrier that orders the other waves' reads).
+  if (wave == 0) {
+    __threadfence();
+    int last = 0;
+    if (lane == 0) last = atomicAdd(done, 1u) == gridDim.x - 1;
+    last = __shfl(last, 0);
+    if (last) __threadfence();
+    if (lane == 0) is_last = last;
+  }
+  __syncthreads();
+  if (!is_last) return;
+  if (wave < n)
+    topk_token<EPL>(logits + (size_t)wave * E, E, k, scale, ids + (size_t)wave * k,
+                    wts + (size_t)wave * k, lane);
+  __syncthreads();
+  sort_block(ids, n * k, E, counts, offsets, perm, inv, bm, tiles, num_tiles, slds);
+  if (tid == 0) *done = 0u;
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 template <int TM>
@@ -639,3 +783,26 @@ hipError_t launch_route_sort(const int* ids, int R, int E, int* counts, int* off
 }
 
 int route_sort_blocks(int R) { return (R + SORT_CH - 1) / SORT_CH; }
+
+hipError_t launch_route_small(const void* hidden, const void* gamma, const void* wgate,
+                              void* normed, void* residual, float* logits, int n, int H, int E,
+                              float eps, int k, float scale, int* ids, float* w, int* counts,
+                              int* offsets, int* perm, int* inv, int bm, int2* tiles,
+                              int* num_tiles, unsigned* done, hipStream_t s) {
+  if (n > 16) return hipErrorInvalidValue;
+  dim3 grid((E + 15) / 16);
+  switch ((E + 63) / 64) {
+#define RS_CASE(X)                                                                            \
+  case X:                                                                                     \
+    hipLaunchKernelGGL((route_small_kernel<X>), grid, dim3(1024), 0, s, (const bf16*)hidden,    \
+                       (const bf16*)gamma, (const bf16*)wgate, (bf16*)normed, (bf16*)residual, \
+                       logits, n, H, E, eps, k, scale, ids, w, counts, offsets, perm, inv, bm,  \
+                       tiles, num_tiles, done);                                               \
+    break;
+    RS_CASE(1) RS_CASE(2) RS_CASE(3) RS_CASE(4) RS_CASE(5) RS_CASE(6) RS_CASE(7) RS_CASE(8)
+#undef RS_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
