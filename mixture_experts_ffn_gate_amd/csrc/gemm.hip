@@ -263,9 +263,10 @@ template <int FT> struct WSrc<1, FT> {
 // ---------------------------------------------------------------------------
 // Persistent MFMA GEMM (grouped or dense), WQ = 0 bf16 weights, 1 NVFP4.
 // ---------------------------------------------------------------------------
+// One output tile: BMT rows x (4 waves x WF) features.
 template <int WF, int BMT, int EPI, typename TC, int WQ, bool GROUPED>
-__global__ void __launch_bounds__(256, (BMT >= 128 ? 2 : 1)) gemm_mfma_kernel(GemmArgs a, int nft, int slots,
-                                                        int wg_per_xcd) {
+__device__ __forceinline__ void mfma_tile(const GemmArgs& a, int slot, int ftile,
+                                          bf16 (&xs)[2][BMT * 64]) {
   constexpr int FT = WF / 16;      // 16-feature tiles per wave
   constexpr int TT = BMT / 16;     // 16-row tiles per workgroup
   constexpr int BK = 64;           // k per step (two MFMA k-chunks of 32)
@@ -273,147 +274,153 @@ __global__ void __launch_bounds__(256, (BMT >= 128 ? 2 : 1)) gemm_mfma_kernel(Ge
   constexpr int LPASS = (CHUNKS + 255) / 256;
   using Src = WSrc<WQ, FT>;
   using Frag = typename Src::Frag;
-  __shared__ __attribute__((aligned(16))) bf16 xs[2][BMT * BK];
-
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nsteps = a.K / BK;
-  // Persistent schedule: workgroup b runs on XCD b % 8 (the dispatcher deals
-  // consecutive workgroups to the 8 XCDs round-robin) and walks that XCD's
-  // items (row tile xcd + 8*j, feature tile f), item = j * nft + f, in steps of
-  // the XCD's workgroup count. Items are row-tile major, so the workgroups of
-  // an XCD work on the feature tiles of the same row tiles (one expert's rows)
-  // at the same time and the XCD's L2 fetches those activation rows once.
-  //   Dense launches (one weight matrix reused by every row tile) deal the
-  // feature tiles to the XCDs instead: XCD x takes feature tiles x + 8*j and
-  // walks all row tiles of each, so each XCD's L2 holds only its own columns
-  // of the weight matrix.
+  TileInfo ti;
+  if (GROUPED) {
+    if (!decode_tile(a, slot, BMT, ti)) return;  // uniform: no barrier skipped
+  } else {
+    ti.g = 0;
+    ti.row0 = slot * BMT;
+    ti.rows = min(BMT, a.M - ti.row0);
+  }
+
+  // Activation loader: chunk c = (tid + 256*i) % CHUNKS -> row c/8, 16-byte
+  // chunk c%8 (small tiles: several threads load the same chunk, so every
+  // load is unconditional and the k-loop has no branches).
+  const bf16* asrc[LPASS];
+  int lds_off[LPASS];
+#pragma unroll
+  for (int i = 0; i < LPASS; ++i) {
+    const int c = (tid + 256 * i) % CHUNKS;
+    const int row = c >> 3, ch = c & 7;
+    const int r = min(row, ti.rows - 1);
+    const int arow = GROUPED ? a_row_of(a, ti.row0 + r) : ti.row0 + r;
+    asrc[i] = (const bf16*)a.A + (size_t)arow * a.lda + ch * 8;
+    lds_off[i] = row * BK + ((ch ^ (row & 7)) << 3);
+  }
+
+  const int nf0 = ftile * (4 * WF) + wave * WF;  // first feature of this wave
+  Src src;
+  src.init(a, ti.g, nf0, lane);
+
+  floatx4 acc[FT][TT];
+#pragma unroll
+  for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) acc[ft][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // Two fragment sets: step ks computes from one while the loads of step
+  // ks+1 land in the other (unrolled by two so both stay live and the loads
+  // issue ahead of the MFMAs).
+  Frag fA, fB;
+  bf16x8 areg[LPASS];
+  src.load(fA, 0);
+#pragma unroll
+  for (int i = 0; i < LPASS; ++i) areg[i] = *(const bf16x8*)(asrc[i]);
+#pragma unroll
+  for (int i = 0; i < LPASS; ++i) *(bf16x8*)(&xs[0][lds_off[i]]) = areg[i];
+  __syncthreads();
+
+  const int brow = lane & 15, bch = lane >> 4;
+  auto compute = [&](int cur, const Frag& w) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      bf16x8 xf[TT];
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        const int row = tt * 16 + brow;
+        const int ch = s * 4 + bch;
+        xf[tt] = *(const bf16x8*)(&xs[cur][row * BK + ((ch ^ (row & 7)) << 3)]);
+      }
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft) {
+        const bf16x8 wf = src.get(w, ft, s, lane);
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+          acc[ft][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf[tt], acc[ft][tt], 0, 0, 0);
+      }
+    }
+  };
+  // One step with the loads of step ks+1 in flight: activations first, then
+  // weights, so the LDS store of the activations waits only for their own
+  // loads and the weight loads stay in flight across the barrier.
+  auto step = [&](int ks, const Frag& wc, Frag& wn) {
+    const int cur = ks & 1;
+#pragma unroll
+    for (int i = 0; i < LPASS; ++i) areg[i] = *(const bf16x8*)(asrc[i] + (ks + 1) * BK);
+    src.load(wn, ks + 1);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
+    compute(cur, wc);
+#pragma unroll
+    for (int i = 0; i < LPASS; ++i) *(bf16x8*)(&xs[cur ^ 1][lds_off[i]]) = areg[i];
+    __syncthreads();
+  };
+
+  int ks = 0;
+  for (; ks + 2 < nsteps; ks += 2) {  // branch-free steady state
+    step(ks, fA, fB);
+    step(ks + 1, fB, fA);
+  }
+  if (ks + 1 < nsteps) {  // two steps left
+    step(ks, fA, fB);
+    compute((ks + 1) & 1, fB);
+  } else {                // one step left
+    compute(ks & 1, fA);
+  }
+
+  // Epilogue: lane holds features nf0 + 16*ft + 4*(lane/16) + 0..3 of row 16*tt + lane%16.
+  const float s2 = WQ == 1 ? a.b_scale2[ti.g] : 1.0f;
+  TC* C = (TC*)a.C;
+#pragma unroll
+  for (int ft = 0; ft < FT; ++ft) {
+    const int n = nf0 + ft * 16 + 4 * (lane >> 4);
+    if (n >= a.N) continue;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const int r = tt * 16 + (lane & 15);
+      if (r >= ti.rows) continue;
+      const int p = ti.row0 + r;
+      floatx4 v = acc[ft][tt];
+      if (WQ == 1) v *= s2;
+      if (EPI == EPI_RELU2) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = relu2(v[q]);
+      }
+      if (EPI == EPI_ADD_RES) {
+        v += store4<TC>::ld((const TC*)a.res + (size_t)p * a.ldc + n);
+        if (a.add) v += store4<TC>::ld((const TC*)a.add + (size_t)p * a.ldc + n);
+      }
+      store4<TC>::st(C + (size_t)p * a.ldc + n, v);
+    }
+  }
+  __syncthreads();  // LDS is reused by the next item
+}
+
+// Persistent schedule: workgroup b runs on XCD b % 8 (the dispatcher deals
+// consecutive workgroups to the 8 XCDs round-robin) and walks that XCD's items
+// in steps of the XCD's workgroup count.
+//  * Grouped items (row tile xcd + 8*j, feature tile f), item = j * nft + f:
+//    row-tile major, so the workgroups of an XCD work on the feature tiles of
+//    the same row tiles (one expert's rows) at the same time and the XCD's L2
+//    fetches those activation rows once.
+//  * Dense items (one weight matrix reused by every row tile): XCD x takes
+//    feature tiles x + 8*j and walks all row tiles of each, so each XCD's L2
+//    holds only its own columns of the weight matrix.
+template <int WF, int BMT, int EPI, typename TC, int WQ, bool GROUPED>
+__global__ void __launch_bounds__(256, (BMT >= 128 ? 2 : 1))
+    gemm_mfma_kernel(GemmArgs a, int nft, int slots, int wg_per_xcd) {
+  __shared__ __attribute__((aligned(16))) bf16 xs[2][BMT * 64];
   const int xcd = blockIdx.x & 7;
   const int live = GROUPED ? min(*a.num_tiles, slots) : slots;
   const int xslots = live > xcd ? (live - xcd + 7) / 8 : 0;
   const int xft = nft > xcd ? (nft - xcd + 7) / 8 : 0;
   const int items = GROUPED ? xslots * nft : xft * slots;
   for (int item = blockIdx.x >> 3; item < items; item += wg_per_xcd) {
-    const int slot = GROUPED ? xcd + 8 * (item / nft) : item % slots;
-    const int ftile = GROUPED ? item % nft : xcd + 8 * (item / slots);
-    TileInfo ti;
-    if (GROUPED) {
-      if (!decode_tile(a, slot, BMT, ti)) continue;
-    } else {
-      ti.g = 0;
-      ti.row0 = slot * BMT;
-      ti.rows = min(BMT, a.M - ti.row0);
-    }
-
-    // Activation loader: chunk c = (tid + 256*i) % CHUNKS -> row c/8, 16-byte
-    // chunk c%8 (small tiles: several threads load the same chunk, so every
-    // load is unconditional and the k-loop has no branches).
-    const bf16* asrc[LPASS];
-    int lds_off[LPASS];
-#pragma unroll
-    for (int i = 0; i < LPASS; ++i) {
-      const int c = (tid + 256 * i) % CHUNKS;
-      const int row = c >> 3, ch = c & 7;
-      const int r = min(row, ti.rows - 1);
-      const int arow = GROUPED ? a_row_of(a, ti.row0 + r) : ti.row0 + r;
-      asrc[i] = (const bf16*)a.A + (size_t)arow * a.lda + ch * 8;
-      lds_off[i] = row * BK + ((ch ^ (row & 7)) << 3);
-    }
-
-    const int nf0 = ftile * (4 * WF) + wave * WF;  // first feature of this wave
-    Src src;
-    src.init(a, ti.g, nf0, lane);
-
-    floatx4 acc[FT][TT];
-#pragma unroll
-    for (int ft = 0; ft < FT; ++ft)
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) acc[ft][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-    // Two fragment sets: step ks computes from one while the loads of step
-    // ks+1 land in the other (unrolled by two so both stay live and the loads
-    // issue ahead of the MFMAs).
-    Frag fA, fB;
-    bf16x8 areg[LPASS];
-    src.load(fA, 0);
-#pragma unroll
-    for (int i = 0; i < LPASS; ++i) areg[i] = *(const bf16x8*)(asrc[i]);
-#pragma unroll
-    for (int i = 0; i < LPASS; ++i) *(bf16x8*)(&xs[0][lds_off[i]]) = areg[i];
-    __syncthreads();
-
-    const int brow = lane & 15, bch = lane >> 4;
-    auto compute = [&](int cur, const Frag& w) {
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        bf16x8 xf[TT];
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-          const int row = tt * 16 + brow;
-          const int ch = s * 4 + bch;
-          xf[tt] = *(const bf16x8*)(&xs[cur][row * BK + ((ch ^ (row & 7)) << 3)]);
-        }
-#pragma unroll
-        for (int ft = 0; ft < FT; ++ft) {
-          const bf16x8 wf = src.get(w, ft, s, lane);
-#pragma unroll
-          for (int tt = 0; tt < TT; ++tt)
-            acc[ft][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf[tt], acc[ft][tt], 0, 0, 0);
-        }
-      }
-    };
-    // One step with the loads of step ks+1 in flight: activations first, then
-    // weights, so the LDS store of the activations waits only for their own
-    // loads and the weight loads stay in flight across the barrier.
-    auto step = [&](int ks, const Frag& wc, Frag& wn) {
-      const int cur = ks & 1;
-#pragma unroll
-      for (int i = 0; i < LPASS; ++i) areg[i] = *(const bf16x8*)(asrc[i] + (ks + 1) * BK);
-      src.load(wn, ks + 1);
-      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
-      compute(cur, wc);
-#pragma unroll
-      for (int i = 0; i < LPASS; ++i) *(bf16x8*)(&xs[cur ^ 1][lds_off[i]]) = areg[i];
-      __syncthreads();
-    };
-
-    int ks = 0;
-    for (; ks + 2 < nsteps; ks += 2) {  // branch-free steady state
-      step(ks, fA, fB);
-      step(ks + 1, fB, fA);
-    }
-    if (ks + 1 < nsteps) {  // two steps left
-      step(ks, fA, fB);
-      compute((ks + 1) & 1, fB);
-    } else {                // one step left
-      compute(ks & 1, fA);
-    }
-
-    // Epilogue: lane holds features nf0 + 16*ft + 4*(lane/16) + 0..3 of row 16*tt + lane%16.
-    const float s2 = WQ == 1 ? a.b_scale2[ti.g] : 1.0f;
-    TC* C = (TC*)a.C;
-#pragma unroll
-    for (int ft = 0; ft < FT; ++ft) {
-      const int n = nf0 + ft * 16 + 4 * (lane >> 4);
-      if (n >= a.N) continue;
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) {
-        const int r = tt * 16 + (lane & 15);
-        if (r >= ti.rows) continue;
-        const int p = ti.row0 + r;
-        floatx4 v = acc[ft][tt];
-        if (WQ == 1) v *= s2;
-        if (EPI == EPI_RELU2) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] = relu2(v[q]);
-        }
-        if (EPI == EPI_ADD_RES) {
-          v += store4<TC>::ld((const TC*)a.res + (size_t)p * a.ldc + n);
-          if (a.add) v += store4<TC>::ld((const TC*)a.add + (size_t)p * a.ldc + n);
-        }
-        store4<TC>::st(C + (size_t)p * a.ldc + n, v);
-      }
-    }
-    __syncthreads();  // LDS is reused by the next item
+    if (GROUPED)
+      mfma_tile<WF, BMT, EPI, TC, WQ, true>(a, xcd + 8 * (item / nft), item % nft, xs);
+    else
+      mfma_tile<WF, BMT, EPI, TC, WQ, false>(a, item % slots, xcd + 8 * (item / slots), xs);
   }
 }
 
@@ -447,39 +454,36 @@ static hipError_t launch_persistent(const GemmArgs& a, int slots, hipStream_t s)
 }
 
 template <int WF, int BMT, int WQ, bool G>
-static hipError_t launch_mfma_shape(const GemmArgs& a, int epi, bool tc_bf16, int slots,
-                                    hipStream_t s) {
-  if (tc_bf16) {
-    switch (epi) {
-      case EPI_RELU2: return launch_persistent<WF, BMT, EPI_RELU2, bf16, WQ, G>(a, slots, s);
-      case EPI_STORE: return launch_persistent<WF, BMT, EPI_STORE, bf16, WQ, G>(a, slots, s);
-      case EPI_ADD_RES:
-        if (G) return hipErrorInvalidValue;  // only the dense fc2 adds residual + shared
-        return launch_persistent<WF, BMT, EPI_ADD_RES, bf16, WQ, false>(a, slots, s);
-      default: return hipErrorInvalidValue;
-    }
+static hipError_t launch_mfma_shape(const GemmArgs& a, int epi, int slots, hipStream_t s) {
+  switch (epi) {
+    case EPI_RELU2: return launch_persistent<WF, BMT, EPI_RELU2, bf16, WQ, G>(a, slots, s);
+    case EPI_STORE: return launch_persistent<WF, BMT, EPI_STORE, bf16, WQ, G>(a, slots, s);
+    case EPI_ADD_RES:  // only the dense fc2 adds residual + shared
+      if (G) return hipErrorInvalidValue;
+      return launch_persistent<WF, BMT, EPI_ADD_RES, bf16, WQ, false>(a, slots, s);
+    default: return hipErrorInvalidValue;
   }
-  return hipErrorInvalidValue;  // bf16 layers keep every intermediate in bf16
 }
 
 template <int WQ, bool G>
-static hipError_t launch_mfma_wq(const GemmArgs& a, MfmaCfg cfg, int epi, bool tc_bf16, int slots,
+static hipError_t launch_mfma_wq(const GemmArgs& a, MfmaCfg cfg, int epi, int slots,
                                  hipStream_t s) {
-  if (cfg.wf == 16 && cfg.bmt == 16) return launch_mfma_shape<16, 16, WQ, G>(a, epi, tc_bf16, slots, s);
-  if (cfg.wf == 32 && cfg.bmt == 32) return launch_mfma_shape<32, 32, WQ, G>(a, epi, tc_bf16, slots, s);
-  if (cfg.wf == 32 && cfg.bmt == 64) return launch_mfma_shape<32, 64, WQ, G>(a, epi, tc_bf16, slots, s);
-  if (cfg.wf == 32 && cfg.bmt == 128) return launch_mfma_shape<32, 128, WQ, G>(a, epi, tc_bf16, slots, s);
+#define SHAPE(W, M) \
+  if (cfg.wf == W && cfg.bmt == M) return launch_mfma_shape<W, M, WQ, G>(a, epi, slots, s);
+  SHAPE(16, 16) SHAPE(32, 32) SHAPE(32, 64) SHAPE(32, 128)
+#undef SHAPE
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm_mfma(const GemmArgs& a, MfmaCfg cfg, int epi, bool tc_bf16, bool nvfp4,
                             int slots, hipStream_t s) {
+  if (!tc_bf16) return hipErrorInvalidValue;  // bf16 layers keep every intermediate in bf16
   const bool g = a.tiles != nullptr;
   if (nvfp4)
-    return g ? launch_mfma_wq<1, true>(a, cfg, epi, tc_bf16, slots, s)
-             : launch_mfma_wq<1, false>(a, cfg, epi, tc_bf16, slots, s);
-  return g ? launch_mfma_wq<0, true>(a, cfg, epi, tc_bf16, slots, s)
-           : launch_mfma_wq<0, false>(a, cfg, epi, tc_bf16, slots, s);
+    return g ? launch_mfma_wq<1, true>(a, cfg, epi, slots, s)
+             : launch_mfma_wq<1, false>(a, cfg, epi, slots, s);
+  return g ? launch_mfma_wq<0, true>(a, cfg, epi, slots, s)
+           : launch_mfma_wq<0, false>(a, cfg, epi, slots, s);
 }
 
 // ---------------------------------------------------------------------------

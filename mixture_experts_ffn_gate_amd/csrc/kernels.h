@@ -65,10 +65,9 @@ hipError_t launch_route_small(const void* hidden, const void* gamma, const void*
 // fp32 SIMT GEMM (64x64 tiles, bm must be 64 in grouped mode); C fp32.
 hipError_t launch_gemm_simt_f32(const GemmArgs& a, int epi, int grid_y, hipStream_t s);
 
-// bf16 MFMA GEMM. cfg selects the tile shape (see gemm.hip); C dtype by epilogue:
-// tc_bf16 = true stores bf16, else fp32.
+// bf16 MFMA GEMM. cfg selects the tile shape; C is bf16 (tc_bf16 must be true).
 struct MfmaCfg {
-  int wf;   // features per wave (16, 32, 64)
+  int wf;   // features per wave (16, 32)
   int bmt;  // rows (tokens / routes) per workgroup tile (16, 32, 64, 128)
 };
 // `slots` = row tiles (grouped: tile-list capacity, live count read on device).

@@ -6,20 +6,21 @@
 // MFMA lane order, and allocates a workspace for max_tokens so that a forward
 // never allocates. moe_layer_forward (same page, `prefill`) enqueues:
 //
-//   norm_gate      RMSNorm + residual save + gate logits          (stream)
-//   shared up/down relu^2 FFN of the shared expert                (side stream)
-//   fc1            latent projection (LatentMoE only)             (stream)
+//   norm_gate      RMSNorm + residual save + gate logits
+//   shared up/down relu^2 FFN of the shared expert (needs only normed)
+//   fc1            latent projection (LatentMoE only)
 //   topk           sigmoid top-k + weights
 //   sort           histogram / prefix sum / stable scatter / tile list
 //   grouped up     gathered rows x up_e, relu^2 epilogue -> h (bf16)
-//   grouped down   h x down_e -> y (fp32, expert-sorted rows)
+//   grouped down   h x down_e -> y (expert-sorted rows)
 //   reduce         direct: hidden = residual + sum_j w*y + shared
 //                  latent: o = sum_j w*y; fc2 GEMM with the residual and
 //                  shared added in its epilogue -> hidden
 //
-// The shared expert does not depend on routing, so it runs on a side stream
-// forked from the caller's stream by an event and joined before the reduce.
-// Nothing reads back to the host.
+// Everything runs in order on the caller's stream: every GEMM launch is a
+// persistent grid that fills the chip, so a concurrent side stream only
+// starves the kernels of the other. Token counts up to 16 take the GEMV arm
+// (forward_small). Nothing reads back to the host.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -97,8 +98,6 @@ struct moe_layer {
   void* y = nullptr;      // routed output [R][D], expert-sorted rows
   void* o = nullptr;      // latent routed sum [N][L]
   std::vector<void*> allocs;
-  hipStream_t side = nullptr;
-  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   int last_n = 0;
   // Stage timing: events[(fwd * MOE_NUM_STAGES + stage) * 2 + {0,1}].
   bool timing = false;
@@ -129,9 +128,6 @@ void free_layer(moe_layer* L) {
   if (!L) return;
   for (void* p : L->allocs) (void)hipFree(p);
   for (hipEvent_t e : L->tev) (void)hipEventDestroy(e);
-  if (L->ev_fork) (void)hipEventDestroy(L->ev_fork);
-  if (L->ev_join) (void)hipEventDestroy(L->ev_join);
-  if (L->side) (void)hipStreamDestroy(L->side);
   delete L;
 }
 
@@ -444,9 +440,6 @@ int moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_weights_t* w
   TRY(dalloc(L, &L->h, R * I * as));
   TRY(dalloc(L, &L->y, R * D * as));
 
-  TRYH(hipStreamCreateWithFlags(&L->side, hipStreamNonBlocking));
-  TRYH(hipEventCreateWithFlags(&L->ev_fork, hipEventDisableTiming));
-  TRYH(hipEventCreateWithFlags(&L->ev_join, hipEventDisableTiming));
   // The norm+gate kernel keeps TM=4 fp32 rows of hidden in LDS.
   TRYH(hipStreamSynchronize(s));
 #undef TRY
@@ -485,29 +478,26 @@ int moe_layer_forward(moe_layer_t* L, void* hidden, void* residual, int32_t n, v
                              L->logits, n, H, E, c.rms_eps, s));
   }
 
-  // 2. Shared expert on the side stream.
+  // 2. Shared expert (needs only the normed rows).
   if (S > 0) {
-    HIP_TRY(hipEventRecord(L->ev_fork, s));
-    HIP_TRY(hipStreamWaitEvent(L->side, L->ev_fork, 0));
     {
-      StageScope sc(L, MOE_STAGE_SHARED_UP, L->side);
+      StageScope sc(L, MOE_STAGE_SHARED_UP, s);
       GemmArgs a{};
       a.A = L->normed; a.lda = H; a.C = L->g_sh; a.ldc = S;
       a.M = n; a.N = S; a.K = H;
       set_weights(L, a, L->sh_up, L->sh_up_s, L->sh_up_s2, S, H);
-      int rc = gemm(L, a, EPI_RELU2, bf, dc, dgrid, L->side, "shared up", L->nvfp4);
+      int rc = gemm(L, a, EPI_RELU2, bf, dc, dgrid, s, "shared up", L->nvfp4);
       if (rc) return rc;
     }
     {
-      StageScope sc(L, MOE_STAGE_SHARED_DOWN, L->side);
+      StageScope sc(L, MOE_STAGE_SHARED_DOWN, s);
       GemmArgs b{};
       b.A = L->g_sh; b.lda = S; b.C = L->sh; b.ldc = H;
       b.M = n; b.N = H; b.K = S;
       set_weights(L, b, L->sh_down, L->sh_down_s, L->sh_down_s2, H, S);
-      int rc = gemm(L, b, EPI_STORE, bf, dc, dgrid, L->side, "shared down", L->nvfp4);
+      int rc = gemm(L, b, EPI_STORE, bf, dc, dgrid, s, "shared down", L->nvfp4);
       if (rc) return rc;
     }
-    HIP_TRY(hipEventRecord(L->ev_join, L->side));
   }
 
   // 3. Latent input.
@@ -558,8 +548,7 @@ int moe_layer_forward(moe_layer_t* L, void* hidden, void* residual, int32_t n, v
     if (rc) return rc;
   }
 
-  // 6. Join the shared expert, reduce, residual.
-  if (S > 0) HIP_TRY(hipStreamWaitEvent(s, L->ev_join, 0));
+  // 6. Reduce, residual.
   if (Lt == 0) {
     StageScope sc(L, MOE_STAGE_REDUCE, s);
     HIP_TRY(launch_unpermute_reduce(c.act_dtype, false, L->y, L->inv, L->w, n, k, D, residual,
