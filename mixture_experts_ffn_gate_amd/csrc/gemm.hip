@@ -33,6 +33,8 @@
 
 #include "kernels.h"
 
+#include <utility>
+
 // ---------------------------------------------------------------------------
 // Tile decode shared by both kernels.
 // ---------------------------------------------------------------------------
@@ -177,17 +179,19 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
 
 // Eight E2M1 codes (nibble i = element i) times an fp32 block scale -> bf16.
 // e2m1 * e4m3 has at most 6 significant bits, so every product is exact in bf16.
+// gfx950 converts two E2M1 codes (byte j: low nibble first) to fp32 per
+// instruction. Its scale operand acts as a power of two only, so it is 1 here
+// and the E4M3 block scale multiplies in fp32.
 __device__ __forceinline__ bf16x8 dequant8(uint32_t q, float sc) {
+  const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 0);
+  const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 1);
+  const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 2);
+  const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 3);
   bf16x8 o;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t c = (q >> (4 * i)) & 15u, mag = c & 7u;
-    // magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6: for mag >= 2 the fp32 bits are
-    // (mag << 22) + (126 << 23); mag 1 is 0.5 and mag 0 is 0.
-    uint32_t bits = mag >= 2u ? (mag << 22) + (126u << 23) : (mag ? (126u << 23) : 0u);
-    bits |= (c & 8u) << 28;
-    o[i] = (bf16)(__uint_as_float(bits) * sc);
-  }
+  o[0] = (bf16)(p0[0] * sc); o[1] = (bf16)(p0[1] * sc);
+  o[2] = (bf16)(p1[0] * sc); o[3] = (bf16)(p1[1] * sc);
+  o[4] = (bf16)(p2[0] * sc); o[5] = (bf16)(p2[1] * sc);
+  o[6] = (bf16)(p3[0] * sc); o[7] = (bf16)(p3[1] * sc);
   return o;
 }
 
@@ -263,10 +267,14 @@ template <int FT> struct WSrc<1, FT> {
 // ---------------------------------------------------------------------------
 // Persistent MFMA GEMM (grouped or dense), WQ = 0 bf16 weights, 1 NVFP4.
 // ---------------------------------------------------------------------------
+// Pipeline depth (k-steps in flight). Three stages measured no faster than
+// two at any tile height here, and cost occupancy at 64-row tiles.
+constexpr int mfma_stages(int) { return 2; }
 // One output tile: BMT rows x (4 waves x WF) features.
 template <int WF, int BMT, int EPI, typename TC, int WQ, bool GROUPED>
 __device__ __forceinline__ void mfma_tile(const GemmArgs& a, int slot, int ftile,
-                                          bf16 (&xs)[2][BMT * 64]) {
+                                          bf16 (&xs)[mfma_stages(BMT)][BMT * 64]) {
+  constexpr int S = mfma_stages(BMT);
   constexpr int FT = WF / 16;      // 16-feature tiles per wave
   constexpr int TT = BMT / 16;     // 16-row tiles per workgroup
   constexpr int BK = 64;           // k per step (two MFMA k-chunks of 32)
@@ -310,20 +318,26 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs& a, int slot, int ftile
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) acc[ft][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // Two fragment sets: step ks computes from one while the loads of step
-  // ks+1 land in the other (unrolled by two so both stay live and the loads
-  // issue ahead of the MFMAs).
-  Frag fA, fB;
+  // S-stage pipeline: the weights of step k+S-1 are loaded (into register set
+  // (k+S-1)%S) while step k computes, so S-1 steps of compute cover their
+  // latency; the activations of step k+S-1 are loaded at the start of step k
+  // and written to LDS slot (k+S-1)%S (consumed at step k-1) after its MFMAs.
+  // The ring index is a compile-time constant: the k-loop is unrolled by S.
+  Frag w[S];
   bf16x8 areg[LPASS];
-  src.load(fA, 0);
 #pragma unroll
-  for (int i = 0; i < LPASS; ++i) areg[i] = *(const bf16x8*)(asrc[i]);
+  for (int p = 0; p < S - 1; ++p) {
+    const int kp = min(p, nsteps - 1);
+    src.load(w[p], kp);
 #pragma unroll
-  for (int i = 0; i < LPASS; ++i) *(bf16x8*)(&xs[0][lds_off[i]]) = areg[i];
+    for (int i = 0; i < LPASS; ++i) areg[i] = *(const bf16x8*)(asrc[i] + kp * BK);
+#pragma unroll
+    for (int i = 0; i < LPASS; ++i) *(bf16x8*)(&xs[p][lds_off[i]]) = areg[i];
+  }
   __syncthreads();
 
   const int brow = lane & 15, bch = lane >> 4;
-  auto compute = [&](int cur, const Frag& w) {
+  auto compute = [&](int cur, const Frag& wc) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       bf16x8 xf[TT];
@@ -335,39 +349,44 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs& a, int slot, int ftile
       }
 #pragma unroll
       for (int ft = 0; ft < FT; ++ft) {
-        const bf16x8 wf = src.get(w, ft, s, lane);
+        const bf16x8 wf = src.get(wc, ft, s, lane);
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt)
           acc[ft][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf[tt], acc[ft][tt], 0, 0, 0);
       }
     }
   };
-  // One step with the loads of step ks+1 in flight: activations first, then
-  // weights, so the LDS store of the activations waits only for their own
-  // loads and the weight loads stay in flight across the barrier.
-  auto step = [&](int ks, const Frag& wc, Frag& wn) {
-    const int cur = ks & 1;
+  // Step k (ring slot u = k % S). PREF: whether step k+S-1 exists (the steady
+  // state always prefetches; only the last S-1 steps of an item skip it).
+  auto step = [&](int k, auto u_c, bool pref) {
+    constexpr int u = decltype(u_c)::value;
+    constexpr int un = (u + S - 1) % S;
+    const int kn = k + S - 1;
+    if (pref) {
 #pragma unroll
-    for (int i = 0; i < LPASS; ++i) areg[i] = *(const bf16x8*)(asrc[i] + (ks + 1) * BK);
-    src.load(wn, ks + 1);
+      for (int i = 0; i < LPASS; ++i) areg[i] = *(const bf16x8*)(asrc[i] + kn * BK);
+      src.load(w[un], kn);
+    }
     __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
-    compute(cur, wc);
+    compute(u, w[u]);
+    if (pref) {
 #pragma unroll
-    for (int i = 0; i < LPASS; ++i) *(bf16x8*)(&xs[cur ^ 1][lds_off[i]]) = areg[i];
+      for (int i = 0; i < LPASS; ++i) *(bf16x8*)(&xs[un][lds_off[i]]) = areg[i];
+    }
     __syncthreads();
   };
-
-  int ks = 0;
-  for (; ks + 2 < nsteps; ks += 2) {  // branch-free steady state
-    step(ks, fA, fB);
-    step(ks + 1, fB, fA);
-  }
-  if (ks + 1 < nsteps) {  // two steps left
-    step(ks, fA, fB);
-    compute((ks + 1) & 1, fB);
-  } else {                // one step left
-    compute(ks & 1, fA);
-  }
+  auto group = [&](int k0, bool tail) {
+    [&]<int... U>(std::integer_sequence<int, U...>) {
+      ((tail ? (k0 + U < nsteps ? step(k0 + U, std::integral_constant<int, U>{},
+                                       k0 + U + S - 1 < nsteps)
+                                : void())
+             : step(k0 + U, std::integral_constant<int, U>{}, true)),
+       ...);
+    }(std::make_integer_sequence<int, S>{});
+  };
+  int k0 = 0;
+  for (; k0 + 2 * S - 1 <= nsteps; k0 += S) group(k0, false);  // no bounds checks
+  for (; k0 < nsteps; k0 += S) group(k0, true);                // at most two groups
 
   // Epilogue: lane holds features nf0 + 16*ft + 4*(lane/16) + 0..3 of row 16*tt + lane%16.
   const float s2 = WQ == 1 ? a.b_scale2[ti.g] : 1.0f;
@@ -410,7 +429,7 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs& a, int slot, int ftile
 template <int WF, int BMT, int EPI, typename TC, int WQ, bool GROUPED>
 __global__ void __launch_bounds__(256, (BMT >= 128 ? 2 : 1))
     gemm_mfma_kernel(GemmArgs a, int nft, int slots, int wg_per_xcd) {
-  __shared__ __attribute__((aligned(16))) bf16 xs[2][BMT * 64];
+  __shared__ __attribute__((aligned(16))) bf16 xs[mfma_stages(BMT)][BMT * 64];
   const int xcd = blockIdx.x & 7;
   const int live = GROUPED ? min(*a.num_tiles, slots) : slots;
   const int xslots = live > xcd ? (live - xcd + 7) / 8 : 0;
