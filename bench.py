@@ -256,7 +256,7 @@ def measured_traffic(wl, stage):
     from mixture_experts_ffn_gate_amd import profiling
 
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                        f"traffic_{wl.name}.json")
+                        f"traffic_{wl.name}_n{wl.N}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
@@ -264,8 +264,12 @@ def measured_traffic(wl, stage):
         return None
     role = "relu2" if stage == "grouped_up" else "store"
     wq = "nvfp4" if wl.expert_dtype == "nvfp4" else "bf16"
+    prefix = (f"gemv[{role},{wq}]" if wl.N <= GEMV_MAX_N and wl.act_dtype == "bf16"
+              else f"gemm[grouped,{role},{wq},")
+    if rec.get("tokens") != wl.N:
+        return None
     cands = [(v.get("dispatches", 0), v) for k, v in rec["kernels"].items()
-             if k.startswith(f"gemm[grouped,{role},{wq},")]
+             if k.startswith(prefix)]
     if not cands:
         return None
     v = max(cands, key=lambda c: c[0])[1]

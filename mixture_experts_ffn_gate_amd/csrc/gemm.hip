@@ -418,28 +418,32 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs& a, int slot, int ftile
 
 // Persistent schedule: workgroup b runs on XCD b % 8 (the dispatcher deals
 // consecutive workgroups to the 8 XCDs round-robin) and walks that XCD's items
-// in steps of the XCD's workgroup count.
-//  * Grouped items (row tile xcd + 8*j, feature tile f), item = j * nft + f:
-//    row-tile major, so the workgroups of an XCD work on the feature tiles of
-//    the same row tiles (one expert's rows) at the same time and the XCD's L2
-//    fetches those activation rows once.
-//  * Dense items (one weight matrix reused by every row tile): XCD x takes
-//    feature tiles x + 8*j and walks all row tiles of each, so each XCD's L2
-//    holds only its own columns of the weight matrix.
+// in steps of the XCD's workgroup count. Each XCD owns a contiguous eighth of
+// the tiles on one axis and walks every tile of the other axis for each:
+//  * Row-major (grouped launches; dense ones whose activation rows outweigh
+//    the weight matrix): XCD x owns row tiles [x*c, (x+1)*c), item = j * nft
+//    + f. The XCD's workgroups run on the feature tiles of a few neighbouring
+//    row tiles at a time, so its L2 fetches those activation rows once, and
+//    the row tiles of one expert (neighbours in the tile list) read each
+//    weight slice at about the same time on the same L2.
+//  * Feature-major (dense launches whose weight matrix is the larger
+//    operand): XCD x owns feature tiles [x*c, (x+1)*c) and walks all row tiles
+//    of each, so its L2 holds only its own columns of the weight matrix.
 template <int WF, int BMT, int EPI, typename TC, int WQ, bool GROUPED>
 __global__ void __launch_bounds__(256, (BMT >= 128 ? 2 : 1))
-    gemm_mfma_kernel(GemmArgs a, int nft, int slots, int wg_per_xcd) {
+    gemm_mfma_kernel(GemmArgs a, int nft, int slots, int wg_per_xcd, int rows_major) {
   __shared__ __attribute__((aligned(16))) bf16 xs[mfma_stages(BMT)][BMT * 64];
   const int xcd = blockIdx.x & 7;
   const int live = GROUPED ? min(*a.num_tiles, slots) : slots;
-  const int xslots = live > xcd ? (live - xcd + 7) / 8 : 0;
-  const int xft = nft > xcd ? (nft - xcd + 7) / 8 : 0;
-  const int items = GROUPED ? xslots * nft : xft * slots;
+  const int outer = rows_major ? live : nft;    // the axis split over the XCDs
+  const int inner = rows_major ? nft : live;    // walked whole by each XCD
+  const int chunk = (outer + 7) / 8;
+  const int o0 = xcd * chunk;
+  const int items = max(0, min(chunk, outer - o0)) * inner;
   for (int item = blockIdx.x >> 3; item < items; item += wg_per_xcd) {
-    if (GROUPED)
-      mfma_tile<WF, BMT, EPI, TC, WQ, true>(a, xcd + 8 * (item / nft), item % nft, xs);
-    else
-      mfma_tile<WF, BMT, EPI, TC, WQ, false>(a, item % slots, xcd + 8 * (item / slots), xs);
+    const int o = o0 + item / inner, i = item % inner;
+    const int slot = rows_major ? o : i, ftile = rows_major ? i : o;
+    mfma_tile<WF, BMT, EPI, TC, WQ, GROUPED>(a, slot, ftile, xs);
   }
 }
 
@@ -465,10 +469,15 @@ static hipError_t launch_persistent(const GemmArgs& a, int slots, hipStream_t s)
     cus = n;
   }
   const int nft = (a.N + 4 * WF - 1) / (4 * WF);
-  const int max_items_per_xcd = GROUPED ? ((slots + 7) / 8) * nft : ((nft + 7) / 8) * slots;
+  // Dense: split the larger operand over the XCDs' L2s.
+  const double wbytes = (double)a.N * a.K * (WQ ? 0.5625 : 2.0);
+  const double abytes = (double)a.M * a.K * 2.0;
+  const int rows_major = GROUPED || abytes > wbytes;
+  const int outer = rows_major ? slots : nft, inner = rows_major ? nft : slots;
+  const int max_items_per_xcd = ((outer + 7) / 8) * inner;
   const int wg_per_xcd = std::max(1, std::min(max_items_per_xcd, (cus / 8) * occ));
   hipLaunchKernelGGL((gemm_mfma_kernel<WF, BMT, EPI, TC, WQ, GROUPED>), dim3(8 * wg_per_xcd),
-                     dim3(256), 0, s, a, nft, slots, wg_per_xcd);
+                     dim3(256), 0, s, a, nft, slots, wg_per_xcd, rows_major);
   return hipGetLastError();
 }
 

@@ -2,14 +2,14 @@
 
     python -m mixture_experts_ffn_gate_amd.profiling stats  STATS_CSV  OUT_MD  --cmd "..."
     python -m mixture_experts_ffn_gate_amd.profiling traffic FETCH_CSV WRITE_CSV OUT_JSON \
-        --calib-mib 512 --workload NAME --cmd "..."
+        --calib-mib 512 --workload NAME --tokens N --cmd "..."
 
 ``traffic`` reads two ``--pmc`` runs (FETCH_SIZE, then WRITE_SIZE; KiB per
 dispatch) of a ``bench.py --calibrate-copy-mib M`` command. The M MiB
 device-to-device copy in the same run gives each counter's scale factor:
 true KiB / counted KiB. The record stores, per layer kernel, the mean scaled
-bytes per dispatch, plus a hash of the GEMM source. ``bench.py`` reports the
-traffic only while that hash matches the current source.
+bytes per dispatch, plus a hash of the kernel and launch sources. ``bench.py``
+reports the traffic only while that hash matches the current source.
 """
 
 from __future__ import annotations
@@ -23,7 +23,7 @@ import re
 from collections import defaultdict
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ("csrc/gemm.hip", "csrc/routing.hip", "csrc/reduce.hip")
+KERNEL_SOURCES = ("csrc/gemm.hip", "csrc/routing.hip", "csrc/reduce.hip", "csrc/layer.cpp")
 
 
 def source_hash() -> str:
@@ -34,21 +34,42 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-_MANGLED = re.compile(r"gemm_mfma_kernelILi(\d+)ELi(\d+)ELi(\d+)E(\w+?)Li(\d+)ELb(\d)E")
-_DEMANGLED = re.compile(r"gemm_mfma_kernel<(\d+), (\d+), (\d+), ([\w ]+), (\d+), (true|false)>")
+_MANGLED = re.compile(r"gemm_mfma_kernelILi(\d+)ELi(\d+)ELi(\d+)E\w+?Li(\d+)ELb(\d)E")
+# The profiler's demangler renders the bf16 argument as "bool _Accum" and an
+# NVFP4 weight flag as "int, E"; it leaves the bf16-weight kernels mangled.
+_DEMANGLED = re.compile(r"gemm_mfma_kernel<(\d+), (\d+), (\d+), (.*), (true|false)>")
+_GEMV_MANGLED = re.compile(r"gemv_kernelILi(\d+)E\w+?Li(\d+)EE")
+_GEMV_DEMANGLED = re.compile(r"gemv_kernel<(\d+), (.*)>")
 _EPI = {"0": "relu2", "1": "store", "2": "add_res"}
+
+
+def _wq(mid: str) -> str:
+    return "bf16" if mid.strip().endswith("0") else "nvfp4"
 
 
 def short_name(name: str) -> str:
     """Readable kernel label; GEMMs by role (grouped/dense, epilogue, weights, tile)."""
-    m = _MANGLED.search(name) or _DEMANGLED.search(name)
+    m = _MANGLED.search(name)
     if m:
-        wf, bmt, epi, _, wq, g = m.groups()
-        grouped = g in ("1", "true")
-        return (f"gemm[{'grouped' if grouped else 'dense'},{_EPI.get(epi, epi)},"
+        wf, bmt, epi, wq, g = m.groups()
+        return (f"gemm[{'grouped' if g == '1' else 'dense'},{_EPI.get(epi, epi)},"
                 f"{'nvfp4' if wq == '1' else 'bf16'},{int(wf) * 4}x{bmt}]")
-    for key in ("norm_gate", "topk_sigmoid", "route_sort", "unpermute_reduce", "retile",
-                "nvfp4_pack", "nvfp4_scale2", "copyBuffer"):
+    m = _DEMANGLED.search(name)
+    if m:
+        wf, bmt, epi, mid, g = m.groups()
+        return (f"gemm[{'grouped' if g == 'true' else 'dense'},{_EPI.get(epi, epi)},"
+                f"{_wq(mid)},{int(wf) * 4}x{bmt}]")
+    m = _GEMV_MANGLED.search(name)
+    if m:
+        epi, wq = m.groups()
+        return f"gemv[{_EPI.get(epi, epi)},{'nvfp4' if wq == '1' else 'bf16'}]"
+    m = _GEMV_DEMANGLED.search(name)
+    if m:
+        epi, mid = m.groups()
+        return f"gemv[{_EPI.get(epi, epi)},{_wq(mid)}]"
+    for key in ("route_small", "norm_gate", "topk_sigmoid", "route_sort", "route_hist",
+                "route_scatter", "unpermute_reduce", "retile", "nvfp4_pack", "nvfp4_scale2",
+                "copyBuffer"):
         if key in name:
             return key
     if "at::native" in name:
@@ -56,17 +77,29 @@ def short_name(name: str) -> str:
     return name[:60]
 
 
+_SETUP = ("torch:", "retile", "nvfp4_pack", "nvfp4_scale2", "copyBuffer", "__amd_rocclr")
+
+
 def stats(csv_path: str, out_md: str, cmd: str) -> None:
+    """Kernel-duration table of the layer's kernels (set-up kernels that build
+    the weights and inputs are left out), slowest total first."""
     rows = list(csv.DictReader(open(csv_path)))
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    layer = [r for r in rows if not short_name(r["Name"]).startswith(_SETUP)]
+    calls = max((int(r["Calls"]) for r in layer), default=0)
+    per_fwd = sum(float(r["TotalDurationNs"]) for r in layer) / max(1, calls) / 1e3
     lines = [f"# Kernel durations: `{os.path.basename(out_md)}`", "",
-             "Command:", "", "```", cmd, "```", "",
+             "Commands (`$REPO` = repository root):", "", "```", cmd, "```", "",
+             "Layer kernels only (weight/input set-up kernels omitted). Every forward",
+             "launches each listed kernel once; the graph-replayed and the eagerly",
+             "timed forwards are both counted.", "",
              "| kernel | symbol (truncated) | calls | avg µs | min µs | max µs |",
              "|---|---|---|---|---|---|"]
-    for r in rows:
+    for r in layer:
         lines.append(f"| {short_name(r['Name'])} | `{r['Name'][:70]}` | {r['Calls']} | "
                      f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} |")
+    lines += ["", f"Sum of the layer kernels' average durations: {per_fwd:.1f} µs per forward."]
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -80,9 +113,9 @@ def _per_dispatch(csv_path: str, counter: str):
 
 
 def traffic(fetch_csv: str, write_csv: str, out_json: str, calib_mib: int, workload: str,
-            cmd: str) -> None:
+            tokens: int, cmd: str) -> None:
     calib_kib = calib_mib * 1024
-    rec = {"workload": workload, "source_hash": source_hash(), "command": cmd,
+    rec = {"workload": workload, "tokens": tokens, "source_hash": source_hash(), "command": cmd,
            "calibration_copy_kib": calib_kib, "kernels": {}}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = _per_dispatch(path, counter)
@@ -119,12 +152,13 @@ def main():
     t.add_argument("out")
     t.add_argument("--calib-mib", type=int, required=True)
     t.add_argument("--workload", required=True)
+    t.add_argument("--tokens", type=int, required=True)
     t.add_argument("--cmd", required=True)
     a = ap.parse_args()
     if a.cmd_name == "stats":
         stats(a.csv, a.out, a.cmd)
     else:
-        traffic(a.fetch_csv, a.write_csv, a.out, a.calib_mib, a.workload, a.cmd)
+        traffic(a.fetch_csv, a.write_csv, a.out, a.calib_mib, a.workload, a.tokens, a.cmd)
 
 
 if __name__ == "__main__":
