@@ -41,9 +41,12 @@ struct GemmArgs {
   const void* add;  // EPI_ADD_RES second addend, C's dtype (may be null)
 };
 
+// RMSNorm + residual + gate logits. wgate_t (bf16 layers, may be null) is the
+// gate matrix re-tiled by launch_retile_bf16 with E padded to a multiple of 16
+// (zero rows); it selects the LDS-staged kernel when 16 rows of H fit in LDS.
 hipError_t launch_norm_gate(int act_dt, const void* hidden, const void* gamma, const void* wgate,
-                            void* normed, void* residual, float* logits, int n, int H, int E,
-                            float eps, hipStream_t s);
+                            const void* wgate_t, void* normed, void* residual, float* logits,
+                            int n, int H, int E, float eps, hipStream_t s);
 hipError_t launch_topk(const float* logits, int n, int E, int k, float scale, int* ids, float* w,
                        hipStream_t s);
 // Stable route sort. With a `bcnt` scratch of route_sort_blocks(R) * E ints

@@ -67,6 +67,7 @@ struct moe_layer {
   // Weights (layer-owned).
   void* gamma = nullptr;
   void* gate = nullptr;
+  void* gate_t = nullptr;  // bf16: gate re-tiled to MFMA lane order, E padded to 16
   void* fc1 = nullptr;
   void* fc2 = nullptr;
   void* up = nullptr;
@@ -121,6 +122,17 @@ int dalloc(moe_layer* L, void** p, size_t bytes) {
     return fail(MOE_ERR_OOM, "hipMalloc(%zu bytes) failed: %s", bytes, hipGetErrorString(e));
   }
   L->allocs.push_back(*p);
+  return MOE_OK;
+}
+
+// Free one allocation made by dalloc (set-up temporaries).
+int dfree(moe_layer* L, void* p) {
+  for (size_t i = 0; i < L->allocs.size(); ++i)
+    if (L->allocs[i] == p) {
+      L->allocs.erase(L->allocs.begin() + i);
+      HIP_TRY(hipFree(p));
+      return MOE_OK;
+    }
   return MOE_OK;
 }
 
@@ -393,6 +405,17 @@ int moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_weights_t* w
   TRYH(hipMemcpyAsync(L->gamma, wts->norm_gamma, H * as, hipMemcpyDeviceToDevice, s));
   TRY(dalloc(L, &L->gate, (size_t)E * H * as));
   TRYH(hipMemcpyAsync(L->gate, wts->gate, (size_t)E * H * as, hipMemcpyDeviceToDevice, s));
+  if (L->mfma) {
+    const size_t e16 = (size_t)(E + 15) / 16 * 16;
+    void* padded = nullptr;
+    TRY(dalloc(L, &padded, e16 * H * 2));
+    TRYH(hipMemsetAsync(padded, 0, e16 * H * 2, s));
+    TRYH(hipMemcpyAsync(padded, wts->gate, (size_t)E * H * 2, hipMemcpyDeviceToDevice, s));
+    TRY(dalloc(L, &L->gate_t, e16 * H * 2));
+    TRYH(launch_retile_bf16((const bf16*)padded, (bf16*)L->gate_t, 1, (int)e16, H, s));
+    TRYH(hipStreamSynchronize(s));
+    TRY(dfree(L, padded));
+  }
   if (Lt > 0) {
     TRY(upload_proj(L, &L->fc1, wts->fc1, 1, Lt, H, L->mfma, s, "fc1"));
     TRY(upload_proj(L, &L->fc2, wts->fc2, 1, H, Lt, L->mfma, s, "fc2"));
@@ -474,8 +497,8 @@ int moe_layer_forward(moe_layer_t* L, void* hidden, void* residual, int32_t n, v
   // 1. RMSNorm + residual + gate logits.
   {
     StageScope sc(L, MOE_STAGE_NORM_GATE, s);
-    HIP_TRY(launch_norm_gate(c.act_dtype, hidden, L->gamma, L->gate, L->normed, residual,
-                             L->logits, n, H, E, c.rms_eps, s));
+    HIP_TRY(launch_norm_gate(c.act_dtype, hidden, L->gamma, L->gate, L->gate_t, L->normed,
+                             residual, L->logits, n, H, E, c.rms_eps, s));
   }
 
   // 2. Shared expert (needs only the normed rows).

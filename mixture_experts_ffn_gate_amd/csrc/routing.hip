@@ -176,8 +176,8 @@ __global__ void __launch_bounds__(256) norm_gate_mfma_kernel(const bf16* __restr
 #pragma unroll
   for (int et = 0; et < ET; ++et) acc[et] = floatx4{0.f, 0.f, 0.f, 0.f};
   const size_t row = (size_t)(t0 + tok) * H + kg * 8;
-  // Four k-steps per round: their loads are issued before any of them is used.
-  constexpr int U = 4;
+  // U k-steps per round: their loads are issued before any of them is used.
+  constexpr int U = ET >= 8 ? 2 : 16 / ET > 8 ? 8 : 16 / ET;
   for (int kb = wave * 32; kb < H; kb += 128 * U) {
     bf16x8 wf[U][ET], xv[U], gv[U];
 #pragma unroll
@@ -568,6 +568,151 @@ __global__ void __launch_bounds__(1024) route_scatter_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// RMSNorm + gate for bf16 layers with the token rows staged in LDS.
+// Block = 8 waves, 16 tokens x ET expert tiles of 16.
+//   1. The 16 hidden rows are read once with contiguous 16-byte loads into
+//      LDS (row stride H + 8 elements: the 16 rows of an MFMA operand read
+//      fall in distinct banks); the residual copy is written on the way and
+//      each wave sums the squares of its rows. gamma is staged as well.
+//   2. Wave w takes expert tile w % ET and the k-steps {j : j % (8/ET) ==
+//      w / ET} of it. The A operand (gate rows) comes from the pre-tiled gate
+//      matrix [E16/16][H/32][64 lanes][8] (one contiguous 1 KiB per wave load);
+//      the B operand is built from LDS: n = x * rinv * gamma in fp32, split
+//      into hi = bf16(n) and lo = bf16(n - hi), two MFMAs per step, so the
+//      logits see ~16 mantissa bits of the fp32 normed value.
+//   3. Partial sums of a tile meet in LDS and are added in fixed order.
+//   Blocks with blockIdx.y == 0 also write normed = bf16(n) from LDS.
+// ---------------------------------------------------------------------------
+// LDS of one block: 16 rows of H + 8, gamma, partial sums, 16 inverse RMS.
+constexpr size_t NG_LDS_MAX = 160 * 1024;
+
+template <int ET>
+__global__ void __launch_bounds__(512) norm_gate_lds_kernel(const bf16* __restrict__ hidden,
+                                                            const bf16* __restrict__ gamma,
+                                                            const bf16* __restrict__ wgate_t,
+                                                            bf16* __restrict__ normed,
+                                                            bf16* __restrict__ residual,
+                                                            float* __restrict__ logits, int n,
+                                                            int H, int E, float eps) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char ng_smem[];
+  constexpr int KS = 8 / ET;  // waves per expert tile (k-split)
+  const int HP = H + 8;
+  bf16* xs = (bf16*)ng_smem;                        // [16][HP]
+  bf16* gs = xs + 16 * HP;                          // [H]
+  floatx4* red = (floatx4*)(gs + H);                // [8][64]
+  float* rinv = (float*)(red + 8 * 64);             // [16]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * 16;
+  const bool writer = blockIdx.y == 0;
+
+  // 1. rows -> LDS (wave w: rows 2w, 2w+1), residual copy, sums of squares
+  for (int i = tid * 8; i < H; i += 512 * 8) *(bf16x8*)(gs + i) = *(const bf16x8*)(gamma + i);
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const int r = wave * 2 + rr;
+    const bool valid = t0 + r < n;
+    const bf16* x = hidden + (size_t)min(t0 + r, n - 1) * H;
+    float ss = 0.f;
+    for (int i0 = lane * 8; i0 < H; i0 += 64 * 8 * 4) {
+      bf16x8 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * 512;
+        v[u] = i < H ? *(const bf16x8*)(x + i) : bf16x8{};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * 512;
+        if (i < H) {
+          *(bf16x8*)(xs + r * HP + i) = v[u];
+          if (writer && valid) *(bf16x8*)(residual + (size_t)(t0 + r) * H + i) = v[u];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const float f = (float)v[u][q];
+            ss += f * f;
+          }
+        }
+      }
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) rinv[r] = 1.0f / sqrtf(ss / (float)H + eps);
+  }
+  __syncthreads();
+
+  // 2. gate: expert tile et = e0/16 + wave % ET, k-steps j = ks, ks + KS, ...
+  const int tok = lane & 15, kg = lane >> 4;
+  const float rv = rinv[tok];
+  const int et = wave % ET, ks = wave / ET;
+  const int tile = blockIdx.y * ET + et;
+  const int nsteps = H / 32;
+  const bf16* wt = wgate_t + ((size_t)tile * nsteps * 64 + lane) * 8;
+  const bf16* xrow = xs + tok * HP + kg * 8;
+  const bf16* grow = gs + kg * 8;
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  constexpr int U = 8;
+  for (int j0 = ks; j0 < nsteps; j0 += KS * U) {
+    bf16x8 wf[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = min(j0 + u * KS, nsteps - 1);  // past the end: a valid step, not used
+      wf[u] = *(const bf16x8*)(wt + (size_t)j * 512);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * KS;
+      if (j >= nsteps) break;
+      const bf16x8 xv = *(const bf16x8*)(xrow + j * 32);
+      const bf16x8 gv = *(const bf16x8*)(grow + j * 32);
+      bf16x8 hi, lo;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float v = (float)xv[q] * rv * (float)gv[q];
+        hi[q] = (bf16)v;
+        lo[q] = (bf16)(v - (float)hi[q]);
+      }
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u], hi, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u], lo, acc, 0, 0, 0);
+    }
+  }
+  red[wave * 64 + lane] = acc;
+
+  // normed rows (writer blocks): wave w rows 2w, 2w+1, from LDS
+  if (writer) {
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const int r = wave * 2 + rr;
+      if (t0 + r >= n) continue;
+      const float rr_inv = rinv[r];
+      for (int i = lane * 8; i < H; i += 512) {
+        const bf16x8 xv = *(const bf16x8*)(xs + r * HP + i);
+        const bf16x8 gv = *(const bf16x8*)(gs + i);
+        bf16x8 o;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) o[q] = (bf16)((float)xv[q] * rr_inv * (float)gv[q]);
+        *(bf16x8*)(normed + (size_t)(t0 + r) * H + i) = o;
+      }
+    }
+  }
+  __syncthreads();
+
+  // 3. tile et's KS partial sums in order (waves et, et + ET, ...)
+  if (wave < ET) {
+    floatx4 v = red[wave * 64 + lane];
+#pragma unroll
+    for (int k2 = 1; k2 < KS; ++k2) v += red[(wave + k2 * ET) * 64 + lane];
+    const int e = (blockIdx.y * ET + wave) * 16 + 4 * kg;
+    if (t0 + tok < n && e < E) {
+      float* dst = logits + (size_t)(t0 + tok) * E + e;
+      if (e + 3 < E && (E & 3) == 0) {
+        *(floatx4*)dst = v;
+      } else {
+        for (int q = 0; q < 4 && e + q < E; ++q) dst[q] = v[q];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Decode-sized routing front end in one launch (N <= 16 tokens, bf16).
 // Block b (16 waves) computes RMSNorm and the gate logits of experts
 // [16b, 16b+16) for all tokens, the k-steps dealt over its 16 waves (same hi+lo
@@ -624,7 +769,7 @@ __global__ void __launch_bounds__(1024) route_small_kernel(
   const bf16* wrow = wgate + (size_t)min(e0 + tok, E - 1) * H + kg * 8;
   const size_t row = (size_t)tok * H + kg * 8;
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-  constexpr int U = 8;
+  constexpr int U = 4;  // 1024-thread blocks: 128 VGPRs per lane at most
   for (int kb = wave * 32; kb < H; kb += 512 * U) {
     bf16x8 wf[U], xv[U], gv[U];
 #pragma unroll
@@ -713,15 +858,46 @@ static void norm_gate_tm(int act_dt, const void* hidden, const void* gamma, cons
 }
 
 hipError_t launch_norm_gate(int act_dt, const void* hidden, const void* gamma, const void* wgate,
-                            void* normed, void* residual, float* logits, int n, int H, int E,
-                            float eps, hipStream_t s) {
+                            const void* wgate_t, void* normed, void* residual, float* logits,
+                            int n, int H, int E, float eps, hipStream_t s) {
+  const size_t lds = (size_t)16 * (H + 8) * 2 + (size_t)H * 2 + 8 * 64 * 16 + 16 * 4;
+  if (act_dt == MOE_DT_BF16 && wgate_t && lds <= NG_LDS_MAX) {
+    // Expert tiles per block: fewer as the token groups shrink, so that the
+    // grid keeps >= 256 blocks where the tiles allow.
+    const int bx = (n + 15) / 16, tiles = (E + 15) / 16;
+    int et = 8;
+    while (et > 1 && (tiles % et != 0 || bx * (tiles / et) < 256)) et /= 2;
+    static bool attr_set = false;  // the dynamic LDS exceeds the 64 KiB default
+    if (!attr_set) {
+      hipError_t e = hipSuccess;
+      const void* fns[4] = {(const void*)norm_gate_lds_kernel<1>, (const void*)norm_gate_lds_kernel<2>,
+                            (const void*)norm_gate_lds_kernel<4>, (const void*)norm_gate_lds_kernel<8>};
+      for (const void* f : fns)
+        if (e == hipSuccess)
+          e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)NG_LDS_MAX);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+    dim3 grid(bx, tiles / et);
+    switch (et) {
+#define NGL_CASE(X)                                                                          \
+  case X:                                                                                    \
+    hipLaunchKernelGGL((norm_gate_lds_kernel<X>), grid, dim3(512), lds, s, (const bf16*)hidden, \
+                       (const bf16*)gamma, (const bf16*)wgate_t, (bf16*)normed,              \
+                       (bf16*)residual, logits, n, H, E, eps);                               \
+    break;
+      NGL_CASE(1) NGL_CASE(2) NGL_CASE(4) NGL_CASE(8)
+#undef NGL_CASE
+    }
+    return hipGetLastError();
+  }
   if (act_dt == MOE_DT_BF16) {
     // 16 tokens per block; split the expert tiles over blockIdx.y until the
     // grid has >= 512 blocks (at least one 16-expert tile per block).
     const int bx = (n + 15) / 16;
     const int tiles = (E + 15) / 16;
     int et = tiles;
-    while (et > 1 && bx * ((tiles + et - 1) / et) < 512) et = (et + 1) / 2;
+    while (et > 1 && bx * ((tiles + et - 1) / et) < 256) et = (et + 1) / 2;
     et = et >= 8 ? 8 : et >= 4 ? 4 : et >= 2 ? 2 : 1;
     dim3 grid(bx, (tiles + et - 1) / et);
     switch (et) {
