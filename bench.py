@@ -47,6 +47,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="nemotron_direct_bf16")
     ap.add_argument("--tokens", type=int, default=None, help="override N of the workload")
+    ap.add_argument("--experts", type=int, default=None,
+                    help="override E of the workload (e.g. one GPU's expert shard)")
     ap.add_argument("--instances", type=int, default=8)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -76,6 +78,8 @@ def main() -> int:
     wl = wlm.WORKLOADS[args.workload]
     if args.tokens:
         wl = wl.with_(N=args.tokens)
+    if args.experts:
+        wl = wl.with_(E=args.experts)
     N = wl.N
     torch.cuda.init()
     dev = torch.device("cuda:0")

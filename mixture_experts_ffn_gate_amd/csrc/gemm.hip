@@ -157,18 +157,16 @@ template <> struct store4<bf16> {
   }
 };
 
-#ifndef MOE_WEIGHT_NT
-#define MOE_WEIGHT_NT 1
-#endif
-// Weights are read exactly once per forward: non-temporal loads stream them
-// past the caches, leaving L2 to the activation rows that are reused.
-template <typename T>
-__device__ __forceinline__ T ld_stream(const T* p) {
-#if MOE_WEIGHT_NT
-  return __builtin_nontemporal_load(p);
-#else
-  return *p;
-#endif
+// Weight loads. A weight byte read once per forward (GEMV arm; grouped GEMMs
+// whose experts fit one row tile) streams past the caches with non-temporal
+// loads. Where the same weights are read once per row tile (dense GEMMs,
+// experts with several row tiles) plain loads let the L2 serve the repeats
+// (measured: the non-temporal hint cost 24% at 8192 tokens and 8% on the
+// latent layer).
+template <bool NT, typename T>
+__device__ __forceinline__ T ld_w(const T* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
 }
 
 // E4M3 (bias 7, no infinities) scale byte -> fp32 (exact).
@@ -203,12 +201,12 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t q, float sc) {
 //    holds the lane's 8 codes of k-chunk s) and block scales
 //    [N/16][K/64][16 rows][4 bytes] (the row's four 16-element blocks of the
 //    step); scale2 of the group multiplies the accumulator in the epilogue.
-template <int WQ, int FT> struct WSrc;
+template <int WQ, int FT, bool NT> struct WSrc;
 
 // Dead tiles (features past N, possible in the last feature tile) keep the
 // loads unconditional but point every lane at one fixed 16-byte chunk with a
 // zero step: one cached line instead of a re-read of live weights.
-template <int FT> struct WSrc<0, FT> {
+template <int FT, bool NT> struct WSrc<0, FT, NT> {
   struct Frag { bf16x8 v[FT][2]; };
   const bf16* p[FT];
   int step[FT];  // elements per 64-wide k-step (0 for a dead tile)
@@ -228,12 +226,12 @@ template <int FT> struct WSrc<0, FT> {
     for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-        f.v[ft][s] = ld_stream((const bf16x8*)(p[ft] + (size_t)ks * step[ft] + s * (step[ft] >> 1)));
+        f.v[ft][s] = ld_w<NT>((const bf16x8*)(p[ft] + (size_t)ks * step[ft] + s * (step[ft] >> 1)));
   }
   __device__ __forceinline__ bf16x8 get(const Frag& f, int ft, int s, int) const { return f.v[ft][s]; }
 };
 
-template <int FT> struct WSrc<1, FT> {
+template <int FT, bool NT> struct WSrc<1, FT, NT> {
   struct Frag { u32x2 q[FT]; uint32_t sc[FT]; };
   const u32x2* pq[FT];
   const uint32_t* ps[FT];
@@ -253,7 +251,7 @@ template <int FT> struct WSrc<1, FT> {
   __device__ __forceinline__ void load(Frag& f, int ks) const {
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) {
-      f.q[ft] = ld_stream(pq[ft] + (size_t)ks * 64 * live[ft]);
+      f.q[ft] = ld_w<NT>(pq[ft] + (size_t)ks * 64 * live[ft]);
       f.sc[ft] = ps[ft][(size_t)ks * 16 * live[ft]];
     }
   }
@@ -271,7 +269,7 @@ template <int FT> struct WSrc<1, FT> {
 // two at any tile height here, and cost occupancy at 64-row tiles.
 constexpr int mfma_stages(int) { return 2; }
 // One output tile: BMT rows x (4 waves x WF) features.
-template <int WF, int BMT, int EPI, typename TC, int WQ, bool GROUPED>
+template <int WF, int BMT, int EPI, typename TC, int WQ, bool GROUPED, bool NT>
 __device__ __forceinline__ void mfma_tile(const GemmArgs& a, int slot, int ftile,
                                           bf16 (&xs)[mfma_stages(BMT)][BMT * 64]) {
   constexpr int S = mfma_stages(BMT);
@@ -280,7 +278,7 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs& a, int slot, int ftile
   constexpr int BK = 64;           // k per step (two MFMA k-chunks of 32)
   constexpr int CHUNKS = BMT * 8;  // 16-byte chunks of one activation slice
   constexpr int LPASS = (CHUNKS + 255) / 256;
-  using Src = WSrc<WQ, FT>;
+  using Src = WSrc<WQ, FT, NT>;
   using Frag = typename Src::Frag;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nsteps = a.K / BK;
@@ -421,15 +419,16 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs& a, int slot, int ftile
 // in steps of the XCD's workgroup count. Each XCD owns a contiguous eighth of
 // the tiles on one axis and walks every tile of the other axis for each:
 //  * Row-major (grouped launches; dense ones whose activation rows outweigh
-//    the weight matrix): XCD x owns row tiles [x*c, (x+1)*c), item = j * nft
-//    + f. The XCD's workgroups run on the feature tiles of a few neighbouring
-//    row tiles at a time, so its L2 fetches those activation rows once, and
-//    the row tiles of one expert (neighbours in the tile list) read each
-//    weight slice at about the same time on the same L2.
+//    the weight matrix): XCD x owns row tiles [x*c, (x+1)*c), taken in groups
+//    of 4 neighbouring row tiles; inside a group the 4 row tiles of one
+//    feature tile are adjacent items. The XCD's workgroups thus run on a few
+//    row tiles at a time (its L2 fetches those activation rows once), and the
+//    row tiles of one expert (neighbours in the tile list) read each weight
+//    slice together, so the L2 serves the repeats.
 //  * Feature-major (dense launches whose weight matrix is the larger
 //    operand): XCD x owns feature tiles [x*c, (x+1)*c) and walks all row tiles
 //    of each, so its L2 holds only its own columns of the weight matrix.
-template <int WF, int BMT, int EPI, typename TC, int WQ, bool GROUPED>
+template <int WF, int BMT, int EPI, typename TC, int WQ, bool GROUPED, bool NT>
 __global__ void __launch_bounds__(256, (BMT >= 128 ? 2 : 1))
     gemm_mfma_kernel(GemmArgs a, int nft, int slots, int wg_per_xcd, int rows_major) {
   __shared__ __attribute__((aligned(16))) bf16 xs[mfma_stages(BMT)][BMT * 64];
@@ -440,20 +439,32 @@ __global__ void __launch_bounds__(256, (BMT >= 128 ? 2 : 1))
   const int chunk = (outer + 7) / 8;
   const int o0 = xcd * chunk;
   const int items = max(0, min(chunk, outer - o0)) * inner;
+  const int nrows = max(0, min(chunk, outer - o0));
   for (int item = blockIdx.x >> 3; item < items; item += wg_per_xcd) {
-    const int o = o0 + item / inner, i = item % inner;
-    const int slot = rows_major ? o : i, ftile = rows_major ? i : o;
-    mfma_tile<WF, BMT, EPI, TC, WQ, GROUPED>(a, slot, ftile, xs);
+    int slot, ftile;
+    if (rows_major) {
+      // groups of RG row tiles; inside a group the RG row tiles of one feature
+      // tile are adjacent items (they read the same weight slice together)
+      constexpr int RG = 4;
+      const int g = item / (RG * inner), rem = item - g * RG * inner;
+      const int rg = min(RG, nrows - g * RG);
+      slot = o0 + g * RG + rem % rg;
+      ftile = rem / rg;
+    } else {
+      slot = item % inner;
+      ftile = o0 + item / inner;
+    }
+    mfma_tile<WF, BMT, EPI, TC, WQ, GROUPED, NT>(a, slot, ftile, xs);
   }
 }
 
-template <int WF, int BMT, int EPI, typename TC, int WQ, bool GROUPED>
+template <int WF, int BMT, int EPI, typename TC, int WQ, bool GROUPED, bool NT>
 static hipError_t launch_persistent(const GemmArgs& a, int slots, hipStream_t s) {
   static int occ = 0;  // resident workgroups per CU (queried once per process)
   if (occ == 0) {
     int o = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &o, (const void*)gemm_mfma_kernel<WF, BMT, EPI, TC, WQ, GROUPED>, 256, 0) !=
+            &o, (const void*)gemm_mfma_kernel<WF, BMT, EPI, TC, WQ, GROUPED, NT>, 256, 0) !=
             hipSuccess ||
         o < 1)
       o = 1;
@@ -476,42 +487,46 @@ static hipError_t launch_persistent(const GemmArgs& a, int slots, hipStream_t s)
   const int outer = rows_major ? slots : nft, inner = rows_major ? nft : slots;
   const int max_items_per_xcd = ((outer + 7) / 8) * inner;
   const int wg_per_xcd = std::max(1, std::min(max_items_per_xcd, (cus / 8) * occ));
-  hipLaunchKernelGGL((gemm_mfma_kernel<WF, BMT, EPI, TC, WQ, GROUPED>), dim3(8 * wg_per_xcd),
+  hipLaunchKernelGGL((gemm_mfma_kernel<WF, BMT, EPI, TC, WQ, GROUPED, NT>), dim3(8 * wg_per_xcd),
                      dim3(256), 0, s, a, nft, slots, wg_per_xcd, rows_major);
   return hipGetLastError();
 }
 
-template <int WF, int BMT, int WQ, bool G>
+template <int WF, int BMT, int WQ, bool G, bool NT>
 static hipError_t launch_mfma_shape(const GemmArgs& a, int epi, int slots, hipStream_t s) {
   switch (epi) {
-    case EPI_RELU2: return launch_persistent<WF, BMT, EPI_RELU2, bf16, WQ, G>(a, slots, s);
-    case EPI_STORE: return launch_persistent<WF, BMT, EPI_STORE, bf16, WQ, G>(a, slots, s);
+    case EPI_RELU2: return launch_persistent<WF, BMT, EPI_RELU2, bf16, WQ, G, NT>(a, slots, s);
+    case EPI_STORE: return launch_persistent<WF, BMT, EPI_STORE, bf16, WQ, G, NT>(a, slots, s);
     case EPI_ADD_RES:  // only the dense fc2 adds residual + shared
       if (G) return hipErrorInvalidValue;
-      return launch_persistent<WF, BMT, EPI_ADD_RES, bf16, WQ, false>(a, slots, s);
+      return launch_persistent<WF, BMT, EPI_ADD_RES, bf16, WQ, false, NT>(a, slots, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int WQ, bool G>
+template <int WQ, bool G, bool NT>
 static hipError_t launch_mfma_wq(const GemmArgs& a, MfmaCfg cfg, int epi, int slots,
                                  hipStream_t s) {
 #define SHAPE(W, M) \
-  if (cfg.wf == W && cfg.bmt == M) return launch_mfma_shape<W, M, WQ, G>(a, epi, slots, s);
+  if (cfg.wf == W && cfg.bmt == M) return launch_mfma_shape<W, M, WQ, G, NT>(a, epi, slots, s);
   SHAPE(16, 16) SHAPE(32, 32) SHAPE(32, 64) SHAPE(32, 128)
 #undef SHAPE
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm_mfma(const GemmArgs& a, MfmaCfg cfg, int epi, bool tc_bf16, bool nvfp4,
-                            int slots, hipStream_t s) {
+                            int slots, bool stream_weights, hipStream_t s) {
   if (!tc_bf16) return hipErrorInvalidValue;  // bf16 layers keep every intermediate in bf16
-  const bool g = a.tiles != nullptr;
-  if (nvfp4)
-    return g ? launch_mfma_wq<1, true>(a, cfg, epi, slots, s)
-             : launch_mfma_wq<1, false>(a, cfg, epi, slots, s);
-  return g ? launch_mfma_wq<0, true>(a, cfg, epi, slots, s)
-           : launch_mfma_wq<0, false>(a, cfg, epi, slots, s);
+  if (a.tiles) {  // grouped
+    if (stream_weights)
+      return nvfp4 ? launch_mfma_wq<1, true, true>(a, cfg, epi, slots, s)
+                   : launch_mfma_wq<0, true, true>(a, cfg, epi, slots, s);
+    return nvfp4 ? launch_mfma_wq<1, true, false>(a, cfg, epi, slots, s)
+                 : launch_mfma_wq<0, true, false>(a, cfg, epi, slots, s);
+  }
+  // dense: every row tile re-reads the matrix, so its loads stay cached
+  return nvfp4 ? launch_mfma_wq<1, false, false>(a, cfg, epi, slots, s)
+               : launch_mfma_wq<0, false, false>(a, cfg, epi, slots, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -537,7 +552,7 @@ struct GemvArgs {
 template <int EPI, typename TC, int WQ>
 __global__ void __launch_bounds__(256) gemv_kernel(GemvArgs g) {
   constexpr int GU = MOE_GEMV_GU;  // k-steps per load group
-  using Src = WSrc<WQ, 1>;
+  using Src = WSrc<WQ, 1, true>;
   using Frag = typename Src::Frag;
   __shared__ floatx4 part[3][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;

@@ -74,8 +74,10 @@ struct MfmaCfg {
   int bmt;  // rows (tokens / routes) per workgroup tile (16, 32, 64, 128)
 };
 // `slots` = row tiles (grouped: tile-list capacity, live count read on device).
+// stream_weights (grouped launches only): non-temporal weight loads, for
+// experts that take one row tile each (every weight byte read once).
 hipError_t launch_gemm_mfma(const GemmArgs& a, MfmaCfg cfg, int epi, bool tc_bf16, bool nvfp4,
-                            int slots, hipStream_t s);
+                            int slots, bool stream_weights, hipStream_t s);
 
 // Decode-sized GEMV arm (row tiles of <= 16 rows, bf16 activations and
 // output): nseg (1 or 2) segments in one launch, each with `slots` row tiles;

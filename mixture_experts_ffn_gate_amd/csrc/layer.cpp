@@ -246,8 +246,8 @@ MfmaCfg dense_cfg(int n) {
 // One GEMM launch. `nvfp4` marks the expert projections of an NVFP4 layer;
 // the caller fills the NVFP4 fields of `a`.
 int gemm(moe_layer* L, const GemmArgs& a, int epi, bool out_bf16, MfmaCfg cfg, int slots,
-         hipStream_t s, const char* what, bool nvfp4 = false) {
-  hipError_t e = L->mfma ? launch_gemm_mfma(a, cfg, epi, out_bf16, nvfp4, slots, s)
+         hipStream_t s, const char* what, bool nvfp4 = false, bool stream_weights = false) {
+  hipError_t e = L->mfma ? launch_gemm_mfma(a, cfg, epi, out_bf16, nvfp4, slots, stream_weights, s)
                          : launch_gemm_simt_f32(a, epi, slots, s);
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
   return MOE_OK;
@@ -548,6 +548,8 @@ int moe_layer_forward(moe_layer_t* L, void* hidden, void* residual, int32_t n, v
                               L->tiles, L->num_tiles, L->bcnt, s));
   }
   const int tiles_cap = (R + bm - 1) / bm + std::min(E, R);
+  // Experts expected to fit one row tile: each weight byte is read once.
+  const bool one_tile = (long long)((R + E - 1) / E) * 4 <= (long long)bm * 3;
 
   // 5. Grouped expert GEMMs.
   {
@@ -557,7 +559,7 @@ int moe_layer_forward(moe_layer_t* L, void* hidden, void* residual, int32_t n, v
     set_weights(L, a, L->up, L->up_s, L->up_s2, I, D);
     a.C = L->h; a.ldc = I; a.N = I; a.K = D;
     a.tiles = L->tiles; a.num_tiles = L->num_tiles; a.offsets = L->offsets; a.bm = bm;
-    int rc = gemm(L, a, EPI_RELU2, bf, gc, tiles_cap, s, "grouped up", L->nvfp4);
+    int rc = gemm(L, a, EPI_RELU2, bf, gc, tiles_cap, s, "grouped up", L->nvfp4, one_tile);
     if (rc) return rc;
   }
   {
@@ -567,7 +569,7 @@ int moe_layer_forward(moe_layer_t* L, void* hidden, void* residual, int32_t n, v
     set_weights(L, b, L->down, L->down_s, L->down_s2, D, I);
     b.C = L->y; b.ldc = D; b.N = D; b.K = I;
     b.tiles = L->tiles; b.num_tiles = L->num_tiles; b.offsets = L->offsets; b.bm = bm;
-    int rc = gemm(L, b, EPI_STORE, bf, gc, tiles_cap, s, "grouped down", L->nvfp4);
+    int rc = gemm(L, b, EPI_STORE, bf, gc, tiles_cap, s, "grouped down", L->nvfp4, one_tile);
     if (rc) return rc;
   }
 

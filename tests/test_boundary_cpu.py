@@ -97,5 +97,9 @@ def test_profile_kernel_labels():
         "gemm[dense,relu2,bf16,128x128]"
     assert short_name("void gemm_mfma_kernel<32, 128, 0, bool _Accum, int, E, true>"
                       "(GemmArgs, int, int, int)") == "gemm[grouped,relu2,nvfp4,128x128]"
+    assert short_name("void gemm_mfma_kernel<32, 128, 0, bool _Accum, int, E, true, false>"
+                      "(GemmArgs, int, int, int)") == "gemm[grouped,relu2,nvfp4,128x128]"
+    assert short_name("_Z16gemm_mfma_kernelILi32ELi64ELi1EDF16bLi0ELb1ELb1EEv8GemmArgsiii") == \
+        "gemm[grouped,store,bf16,128x64,nt]"
     assert short_name("_Z11gemv_kernelILi1EDF16bLi0EEv8GemvArgs") == "gemv[store,bf16]"
     assert short_name("void route_small_kernel<2>(bool _Accum const*)") == "route_small"
