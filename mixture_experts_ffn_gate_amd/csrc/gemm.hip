@@ -268,16 +268,18 @@ template <int FT, bool NT> struct WSrc<1, FT, NT> {
 // Pipeline depth (k-steps in flight). Three stages measured no faster than
 // two at any tile height here, and cost occupancy at 64-row tiles.
 constexpr int mfma_stages(int) { return 2; }
+
 // One output tile: BMT rows x (4 waves x WF) features.
-template <int WF, int BMT, int EPI, typename TC, int WQ, bool GROUPED, bool NT>
+template <int WF, int BMT, int NW, int EPI, typename TC, int WQ, bool GROUPED, bool NT>
 __device__ __forceinline__ void mfma_tile(const GemmArgs& a, int slot, int ftile,
                                           bf16 (&xs)[mfma_stages(BMT)][BMT * 64]) {
   constexpr int S = mfma_stages(BMT);
   constexpr int FT = WF / 16;      // 16-feature tiles per wave
   constexpr int TT = BMT / 16;     // 16-row tiles per workgroup
   constexpr int BK = 64;           // k per step (two MFMA k-chunks of 32)
+  constexpr int NTHR = NW * 64;    // threads
   constexpr int CHUNKS = BMT * 8;  // 16-byte chunks of one activation slice
-  constexpr int LPASS = (CHUNKS + 255) / 256;
+  constexpr int LPASS = (CHUNKS + NTHR - 1) / NTHR;
   using Src = WSrc<WQ, FT, NT>;
   using Frag = typename Src::Frag;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -291,14 +293,14 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs& a, int slot, int ftile
     ti.rows = min(BMT, a.M - ti.row0);
   }
 
-  // Activation loader: chunk c = (tid + 256*i) % CHUNKS -> row c/8, 16-byte
-  // chunk c%8 (small tiles: several threads load the same chunk, so every
-  // load is unconditional and the k-loop has no branches).
+  // Activation loader: chunk c = (tid + threads*i) % CHUNKS -> row c/8,
+  // 16-byte chunk c%8 (small tiles: several threads load the same chunk, so
+  // every load is unconditional and the k-loop has no branches).
   const bf16* asrc[LPASS];
   int lds_off[LPASS];
 #pragma unroll
   for (int i = 0; i < LPASS; ++i) {
-    const int c = (tid + 256 * i) % CHUNKS;
+    const int c = (tid + NTHR * i) % CHUNKS;
     const int row = c >> 3, ch = c & 7;
     const int r = min(row, ti.rows - 1);
     const int arow = GROUPED ? a_row_of(a, ti.row0 + r) : ti.row0 + r;
@@ -306,7 +308,7 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs& a, int slot, int ftile
     lds_off[i] = row * BK + ((ch ^ (row & 7)) << 3);
   }
 
-  const int nf0 = ftile * (4 * WF) + wave * WF;  // first feature of this wave
+  const int nf0 = ftile * (NW * WF) + wave * WF;  // first feature of this wave
   Src src;
   src.init(a, ti.g, nf0, lane);
 
@@ -428,8 +430,8 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs& a, int slot, int ftile
 //  * Feature-major (dense launches whose weight matrix is the larger
 //    operand): XCD x owns feature tiles [x*c, (x+1)*c) and walks all row tiles
 //    of each, so its L2 holds only its own columns of the weight matrix.
-template <int WF, int BMT, int EPI, typename TC, int WQ, bool GROUPED, bool NT>
-__global__ void __launch_bounds__(256, (BMT >= 128 ? 2 : 1))
+template <int WF, int BMT, int NW, int EPI, typename TC, int WQ, bool GROUPED, bool NT>
+__global__ void __launch_bounds__(NW * 64, (BMT >= 128 && NW == 4 ? 2 : 1))
     gemm_mfma_kernel(GemmArgs a, int nft, int slots, int wg_per_xcd, int rows_major) {
   __shared__ __attribute__((aligned(16))) bf16 xs[mfma_stages(BMT)][BMT * 64];
   const int xcd = blockIdx.x & 7;
@@ -454,17 +456,18 @@ __global__ void __launch_bounds__(256, (BMT >= 128 ? 2 : 1))
       slot = item % inner;
       ftile = o0 + item / inner;
     }
-    mfma_tile<WF, BMT, EPI, TC, WQ, GROUPED, NT>(a, slot, ftile, xs);
+    mfma_tile<WF, BMT, NW, EPI, TC, WQ, GROUPED, NT>(a, slot, ftile, xs);
   }
 }
 
-template <int WF, int BMT, int EPI, typename TC, int WQ, bool GROUPED, bool NT>
+template <int WF, int BMT, int NW, int EPI, typename TC, int WQ, bool GROUPED, bool NT>
 static hipError_t launch_persistent(const GemmArgs& a, int slots, hipStream_t s) {
   static int occ = 0;  // resident workgroups per CU (queried once per process)
   if (occ == 0) {
     int o = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &o, (const void*)gemm_mfma_kernel<WF, BMT, EPI, TC, WQ, GROUPED, NT>, 256, 0) !=
+            &o, (const void*)gemm_mfma_kernel<WF, BMT, NW, EPI, TC, WQ, GROUPED, NT>, NW * 64,
+            0) !=
             hipSuccess ||
         o < 1)
       o = 1;
@@ -479,7 +482,7 @@ static hipError_t launch_persistent(const GemmArgs& a, int slots, hipStream_t s)
       n = 256;
     cus = n;
   }
-  const int nft = (a.N + 4 * WF - 1) / (4 * WF);
+  const int nft = (a.N + NW * WF - 1) / (NW * WF);
   // Dense: split the larger operand over the XCDs' L2s.
   const double wbytes = (double)a.N * a.K * (WQ ? 0.5625 : 2.0);
   const double abytes = (double)a.M * a.K * 2.0;
@@ -487,29 +490,48 @@ static hipError_t launch_persistent(const GemmArgs& a, int slots, hipStream_t s)
   const int outer = rows_major ? slots : nft, inner = rows_major ? nft : slots;
   const int max_items_per_xcd = ((outer + 7) / 8) * inner;
   const int wg_per_xcd = std::max(1, std::min(max_items_per_xcd, (cus / 8) * occ));
-  hipLaunchKernelGGL((gemm_mfma_kernel<WF, BMT, EPI, TC, WQ, GROUPED, NT>), dim3(8 * wg_per_xcd),
-                     dim3(256), 0, s, a, nft, slots, wg_per_xcd, rows_major);
+  hipLaunchKernelGGL((gemm_mfma_kernel<WF, BMT, NW, EPI, TC, WQ, GROUPED, NT>),
+                     dim3(8 * wg_per_xcd), dim3(NW * 64), 0, s, a, nft, slots, wg_per_xcd,
+                     rows_major);
   return hipGetLastError();
 }
 
-template <int WF, int BMT, int WQ, bool G, bool NT>
+template <int WF, int BMT, int NW, int WQ, bool G, bool NT>
 static hipError_t launch_mfma_shape(const GemmArgs& a, int epi, int slots, hipStream_t s) {
   switch (epi) {
-    case EPI_RELU2: return launch_persistent<WF, BMT, EPI_RELU2, bf16, WQ, G, NT>(a, slots, s);
-    case EPI_STORE: return launch_persistent<WF, BMT, EPI_STORE, bf16, WQ, G, NT>(a, slots, s);
+    case EPI_RELU2: return launch_persistent<WF, BMT, NW, EPI_RELU2, bf16, WQ, G, NT>(a, slots, s);
+    case EPI_STORE: return launch_persistent<WF, BMT, NW, EPI_STORE, bf16, WQ, G, NT>(a, slots, s);
     case EPI_ADD_RES:  // only the dense fc2 adds residual + shared
       if (G) return hipErrorInvalidValue;
-      return launch_persistent<WF, BMT, EPI_ADD_RES, bf16, WQ, false, NT>(a, slots, s);
+      return launch_persistent<WF, BMT, NW, EPI_ADD_RES, bf16, WQ, false, NT>(a, slots, s);
     default: return hipErrorInvalidValue;
   }
 }
 
+// bf16 128-row tiles take 8 waves (128 x 256 outputs per workgroup: a
+// quarter less L1 traffic per MFMA) when that still gives every CU two tiles
+// or more; smaller launches keep 4 waves so that more CUs get work. NVFP4
+// weights bring a quarter of the bytes, and measured faster with 4 waves.
 template <int WQ, bool G, bool NT>
 static hipError_t launch_mfma_wq(const GemmArgs& a, MfmaCfg cfg, int epi, int slots,
                                  hipStream_t s) {
+  if (cfg.wf == 32 && cfg.bmt == 128) {
+    static int cus = 0;
+    if (cus == 0) {
+      int dev = 0, n = 0;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        n = 256;
+      cus = n;
+    }
+    const long long items8 = (long long)slots * ((a.N + 255) / 256);
+    if (WQ == 0 && items8 >= 2LL * cus)
+      return launch_mfma_shape<32, 128, 8, WQ, G, NT>(a, epi, slots, s);
+    return launch_mfma_shape<32, 128, 4, WQ, G, NT>(a, epi, slots, s);
+  }
 #define SHAPE(W, M) \
-  if (cfg.wf == W && cfg.bmt == M) return launch_mfma_shape<W, M, WQ, G, NT>(a, epi, slots, s);
-  SHAPE(16, 16) SHAPE(32, 32) SHAPE(32, 64) SHAPE(32, 128)
+  if (cfg.wf == W && cfg.bmt == M) return launch_mfma_shape<W, M, 4, WQ, G, NT>(a, epi, slots, s);
+  SHAPE(16, 16) SHAPE(32, 32) SHAPE(32, 64)
 #undef SHAPE
   return hipErrorInvalidValue;
 }

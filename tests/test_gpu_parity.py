@@ -294,6 +294,19 @@ def test_full_size_sampled(ml, name):
     print("errors", pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"], rows=rows))
 
 
+def test_wide_tiles_sampled(ml):
+    # 128-row tiles with 8 waves per workgroup (grouped up: 1024 rows per
+    # expert; shared up: 32 row tiles x 16 feature tiles) next to 4-wave
+    # ones (the 256-wide down projections). All ids, sampled output rows.
+    wl = wlm.Workload("wide_tiles", H=256, E=8, k=2, I=2048, S=4096, L=0, N=4096)
+    r = run_layer(ml, wl, wl.N, seed=5)
+    Wn = pu.oracle_weights(r["W"])
+    ref_ids, margin, _ = pu.oracle_routing(r["x"], Wn, wl)
+    pu.check_ids(r["ids"], ref_ids, margin)
+    rows = _sample_rows(wl.N, 48, 2)
+    print("errors", pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"], rows=rows))
+
+
 NVFP4_SMALL = {
     "nvfp4_direct": wlm.Workload("nvfp4_direct_s", H=512, E=16, k=4, I=192, S=320, L=0, N=150,
                                  expert_dtype="nvfp4"),
