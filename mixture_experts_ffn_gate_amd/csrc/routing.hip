@@ -734,30 +734,15 @@ __global__ void __launch_bounds__(1024) route_small_kernel(
   __shared__ float rinv[16];
   __shared__ floatx4 red[16][64];
   __shared__ SortLds slds;
+  __shared__ int sids[16 * MOE_MAX_TOPK_REDUCE];
   __shared__ int is_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int e0 = blockIdx.x * 16;
 
   // 1. inverse RMS: wave t takes token t
   {
-    float ss = 0.f;
-    if (wave < n) {
-      const bf16* x = hidden + (size_t)wave * H;
-      for (int i0 = lane * 8; i0 < H; i0 += 512 * 4) {
-        bf16x8 v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = i0 + u * 512 < H ? *(const bf16x8*)(x + i0 + u * 512) : bf16x8{};
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const float f = (float)v[u][q];
-            ss += f * f;
-          }
-      }
-    }
-    ss = wave_sum(ss);
-    if (lane == 0) rinv[wave] = 1.0f / sqrtf(ss / (float)H + eps);
+    const float r = rms_inv_row(hidden + (size_t)min(wave, n - 1) * H, H, eps, lane);
+    if (lane == 0) rinv[wave] = r;
   }
   __syncthreads();
 
@@ -824,11 +809,14 @@ __global__ void __launch_bounds__(1024) route_small_kernel(
   }
   __syncthreads();
   if (!is_last) return;
+  // The ids stay in LDS for the sort (no global round trip), and are copied
+  // out on the side.
   if (wave < n)
-    topk_token<EPL>(logits + (size_t)wave * E, E, k, scale, ids + (size_t)wave * k,
+    topk_token<EPL>(logits + (size_t)wave * E, E, k, scale, sids + wave * k,
                     wts + (size_t)wave * k, lane);
   __syncthreads();
-  sort_block(ids, n * k, E, counts, offsets, perm, inv, bm, tiles, num_tiles, slds);
+  if (tid < n * k) ids[tid] = sids[tid];
+  sort_block(sids, n * k, E, counts, offsets, perm, inv, bm, tiles, num_tiles, slds);
   if (tid == 0) *done = 0u;
 }
 

@@ -39,8 +39,8 @@ _MANGLED = re.compile(r"gemm_mfma_kernelILi(\d+)ELi(\d+)ELi(\d+)E\w+?Li(\d+)ELb(
 # NVFP4 weight flag as "int, E"; it leaves the bf16-weight kernels mangled.
 _DEMANGLED = re.compile(
     r"gemm_mfma_kernel<(\d+), (\d+), (\d+), (.*?), (true|false)(?:, (true|false))?>")
-_GEMV_MANGLED = re.compile(r"gemv_kernelILi(\d+)E\w+?Li(\d+)EE")
-_GEMV_DEMANGLED = re.compile(r"gemv_kernel<(\d+), (.*)>")
+_GEMV_MANGLED = re.compile(r"gemv_kernelILi(\d+)E\w+?Li(\d+)EE()")
+_GEMV_DEMANGLED = re.compile(r"gemv_kernel<(\d+), (.*)>()")
 _EPI = {"0": "relu2", "1": "store", "2": "add_res"}
 
 
@@ -63,11 +63,11 @@ def short_name(name: str) -> str:
                 f"{_wq(mid)},{int(wf) * 4}x{bmt}{',nt' if nt == 'true' else ''}]")
     m = _GEMV_MANGLED.search(name)
     if m:
-        epi, wq = m.groups()
+        epi, wq, norm = m.groups()
         return f"gemv[{_EPI.get(epi, epi)},{'nvfp4' if wq == '1' else 'bf16'}]"
     m = _GEMV_DEMANGLED.search(name)
     if m:
-        epi, mid = m.groups()
+        epi, mid, norm = m.groups()
         return f"gemv[{_EPI.get(epi, epi)},{_wq(mid)}]"
     for key in ("route_small", "norm_gate", "topk_sigmoid", "route_sort", "route_hist",
                 "route_scatter", "unpermute_reduce", "retile", "nvfp4_pack", "nvfp4_scale2",

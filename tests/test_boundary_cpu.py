@@ -102,4 +102,5 @@ def test_profile_kernel_labels():
     assert short_name("_Z16gemm_mfma_kernelILi32ELi64ELi1EDF16bLi0ELb1ELb1EEv8GemmArgsiii") == \
         "gemm[grouped,store,bf16,128x64,nt]"
     assert short_name("_Z11gemv_kernelILi1EDF16bLi0EEv8GemvArgs") == "gemv[store,bf16]"
+    assert short_name("_Z11gemv_kernelILi1EDF16bLi1EEv8GemvArgs") == "gemv[store,nvfp4]"
     assert short_name("void route_small_kernel<2>(bool _Accum const*)") == "route_small"

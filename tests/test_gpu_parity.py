@@ -132,6 +132,8 @@ SMALL = {
     "no_shared": wlm.Workload("no_shared", H=256, E=8, k=2, I=128, S=0, L=0, N=200),
     "topk_all": wlm.Workload("topk_all", H=256, E=8, k=8, I=64, S=64, L=0, N=40),
     "many_rows": wlm.Workload("many_rows", H=256, E=4, k=2, I=128, S=128, L=0, N=700),
+    # E not a multiple of 16 (gate padded with zero rows), H not of 128
+    "odd_experts": wlm.Workload("odd_experts", H=320, E=20, k=3, I=128, S=64, L=0, N=90),
 }
 
 
@@ -149,6 +151,15 @@ def test_small_bf16(ml, name):
     r = run_layer(ml, wl, wl.N, seed=5)
     Wn = pu.oracle_weights(r["W"])
     print("errors", pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"]))
+
+
+@pytest.mark.parametrize("n", [1, 7])
+def test_odd_experts_decode_sizes(ml, n):
+    # decode-size routing kernel with a partial last expert tile
+    wl = SMALL["odd_experts"]
+    r = run_layer(ml, wl, n, seed=12, max_tokens=32)
+    Wn = pu.oracle_weights(r["W"])
+    pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"])
 
 
 @pytest.mark.parametrize("n", [1, 2, 3, 16, 17, 64])
@@ -266,6 +277,38 @@ def test_graph_capture_replays_match_eager(ml):
     for rep in range(3):
         hbuf.copy_(h0)
         junk = torch.randn(1000, device="cuda").sum()  # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(hbuf, eager), f"replay {rep}"
+        assert torch.equal(rbuf, h0)
+        del junk
+
+
+def test_graph_capture_decode_arm(ml):
+    # The decode-sized arm (one routing kernel whose last block re-arms a
+    # device counter, GEMV launches) captured whole: replays must match the
+    # eager run.
+    wl = SMALL["direct_ragged"]
+    n = 5
+    W = wlm.make_weights(wl, 9, "cuda")
+    h0, _ = wlm.make_hidden(wl, n, 9, "cuda")
+    layer = ml.layer_from_workload(wl, W, max_tokens=n)
+    eager = h0.clone()
+    res = torch.empty_like(eager)
+    layer.forward(eager, res)
+    torch.cuda.synchronize()
+    hbuf = h0.clone()
+    rbuf = torch.empty_like(hbuf)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            layer.forward(hbuf, rbuf, stream=s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        hbuf.copy_(h0)
+        junk = torch.randn(1000, device="cuda").sum()
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(hbuf, eager), f"replay {rep}"
