@@ -91,16 +91,12 @@ def test_fp32_layers_accept_multiples_of_16(mod):
 def test_profile_kernel_labels():
     # Labels of the rocprofv3 summaries: mangled and demangled symbol forms.
     from mixture_experts_ffn_gate_amd.profiling import short_name
-    assert short_name("_Z16gemm_mfma_kernelILi32ELi64ELi1EDF16bLi0ELb1EEv8GemmArgsiii") == \
-        "gemm[grouped,store,bf16,128x64]"
-    assert short_name("_Z16gemm_mfma_kernelILi32ELi128ELi0EDF16bLi0ELb0EEv8GemmArgsiii") == \
-        "gemm[dense,relu2,bf16,128x128]"
-    assert short_name("void gemm_mfma_kernel<32, 128, 0, bool _Accum, int, E, true>"
-                      "(GemmArgs, int, int, int)") == "gemm[grouped,relu2,nvfp4,128x128]"
-    assert short_name("void gemm_mfma_kernel<32, 128, 0, bool _Accum, int, E, true, false>"
-                      "(GemmArgs, int, int, int)") == "gemm[grouped,relu2,nvfp4,128x128]"
-    assert short_name("_Z16gemm_mfma_kernelILi32ELi64ELi1EDF16bLi0ELb1ELb1EEv8GemmArgsiii") == \
-        "gemm[grouped,store,bf16,128x64,nt]"
+    assert short_name("_Z16gemm_mfma_kernelILi32ELi64ELi4ELi1EDF16bLi0ELb1ELb1EEv8GemmArgsiiii") \
+        == "gemm[grouped,store,bf16,128x64,nt]"
+    assert short_name("_Z16gemm_mfma_kernelILi32ELi128ELi8ELi0EDF16bLi0ELb0ELb0EEv8GemmArgsiiii") \
+        == "gemm[dense,relu2,bf16,256x128]"
+    assert short_name("void gemm_mfma_kernel<32, 128, 4, 0, bool _Accum, int, E, true, false>"
+                      "(GemmArgs, int, int, int, int)") == "gemm[grouped,relu2,nvfp4,128x128]"
     assert short_name("_Z11gemv_kernelILi1EDF16bLi0EEv8GemvArgs") == "gemv[store,bf16]"
     assert short_name("_Z11gemv_kernelILi1EDF16bLi1EEv8GemvArgs") == "gemv[store,nvfp4]"
     assert short_name("void route_small_kernel<2>(bool _Accum const*)") == "route_small"
