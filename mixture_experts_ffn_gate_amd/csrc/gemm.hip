@@ -415,12 +415,17 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs& a, int slot, int ftile
         *(bf16x4*)(&xs[r * SP + c]) = o;
       }
     __syncthreads();
+    // Grouped outputs (h, y: tens of MB) are stored non-temporally: plain
+    // stores mixed into the weight stream cost 6% more at the bench size.
     const int n0 = ftile * CW;
     for (int q = tid; q < BMT * (CW / 8); q += NTHR) {
       const int r = q / (CW / 8), c = (q % (CW / 8)) * 8;
-      if (r < ti.rows && n0 + c < a.N)
-        *(bf16x8*)((bf16*)C + (size_t)(ti.row0 + r) * a.ldc + n0 + c) =
-            *(const bf16x8*)(&xs[r * SP + c]);
+      if (r < ti.rows && n0 + c < a.N) {
+        bf16x8* dst = (bf16x8*)((bf16*)C + (size_t)(ti.row0 + r) * a.ldc + n0 + c);
+        const bf16x8 v = *(const bf16x8*)(&xs[r * SP + c]);
+        if constexpr (GROUPED) __builtin_nontemporal_store(v, dst);
+        else *dst = v;
+      }
     }
   } else {
 #pragma unroll
