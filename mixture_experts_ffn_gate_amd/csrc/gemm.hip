@@ -642,6 +642,7 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemvArgs g) {
       x[u][0] = *(const bf16x8*)(xp + ks * 64);
       x[u][1] = *(const bf16x8*)(xp + ks * 64 + 32);
     }
+    __builtin_amdgcn_sched_barrier(0);  // all GU steps' loads issue before any MFMA
 #pragma unroll
     for (int u = 0; u < GU; ++u) {
       if (kb + u >= s1) break;

@@ -754,7 +754,7 @@ __global__ void __launch_bounds__(1024) route_small_kernel(
   const bf16* wrow = wgate + (size_t)min(e0 + tok, E - 1) * H + kg * 8;
   const size_t row = (size_t)tok * H + kg * 8;
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-  constexpr int U = 4;  // 1024-thread blocks: 128 VGPRs per lane at most
+  constexpr int U = 6;  // 84 k-steps of H = 2688 in one round (<= 128 VGPRs per lane)
   for (int kb = wave * 32; kb < H; kb += 512 * U) {
     bf16x8 wf[U], xv[U], gv[U];
 #pragma unroll
