@@ -7,7 +7,8 @@
 // never allocates. moe_layer_forward (same page, `prefill`) enqueues:
 //
 //   norm_gate      RMSNorm + residual save + gate logits
-//   shared up/down relu^2 FFN of the shared expert (needs only normed)
+//   shared up/down relu^2 FFN of the shared expert (needs only normed;
+//                  side stream, see below)
 //   fc1            latent projection (LatentMoE only)
 //   topk           sigmoid top-k + weights
 //   sort           histogram / prefix sum / stable scatter / tile list
@@ -17,10 +18,12 @@
 //                  latent: o = sum_j w*y; fc2 GEMM with the residual and
 //                  shared added in its epilogue -> hidden
 //
-// Everything runs in order on the caller's stream: every GEMM launch is a
-// persistent grid that fills the chip, so a concurrent side stream only
-// starves the kernels of the other. Token counts up to 16 take the GEMV arm
-// (forward_small). Nothing reads back to the host.
+// The shared expert runs on a side stream forked by an event after norm_gate
+// and joined before the grouped GEMMs: it overlaps fc1, top-k and the sort,
+// which leave CUs free, but not the grouped GEMMs, whose persistent grids fill
+// the chip (a concurrent launch there only starves the other). Token counts up
+// to 16 take the GEMV arm (forward_small), all on the caller's stream. Nothing
+// reads back to the host.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -92,6 +95,8 @@ struct moe_layer {
   int* num_tiles = nullptr;
   int* bcnt = nullptr;    // per-block expert counts of the multi-block sort
   unsigned* sync = nullptr;  // zeroed counter of the decode-sized routing (left at zero)
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   void* g_sh = nullptr;   // shared-expert activation [N][S]
   void* sh = nullptr;     // shared-expert output [N][H]
   void* z = nullptr;      // latent input [N][L]
@@ -138,6 +143,9 @@ int dfree(moe_layer* L, void* p) {
 
 void free_layer(moe_layer* L) {
   if (!L) return;
+  if (L->ev_fork) (void)hipEventDestroy(L->ev_fork);
+  if (L->ev_join) (void)hipEventDestroy(L->ev_join);
+  if (L->side) (void)hipStreamDestroy(L->side);
   for (void* p : L->allocs) (void)hipFree(p);
   for (hipEvent_t e : L->tev) (void)hipEventDestroy(e);
   delete L;
@@ -451,6 +459,11 @@ int moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_weights_t* w
   TRY(dalloc(L, (void**)&L->num_tiles, 16));
   TRY(dalloc(L, (void**)&L->bcnt, (size_t)route_sort_blocks((int)R) * E * 4));
   TRY(dalloc(L, (void**)&L->sync, kSyncWords * 4));
+  if (L->mfma) {  // the shared expert's stream (default priority) and its events
+    TRYH(hipStreamCreateWithFlags(&L->side, hipStreamNonBlocking));
+    TRYH(hipEventCreateWithFlags(&L->ev_fork, hipEventDisableTiming));
+    TRYH(hipEventCreateWithFlags(&L->ev_join, hipEventDisableTiming));
+  }
   TRYH(hipMemsetAsync(L->sync, 0, kSyncWords * 4, s));
   if (S > 0) {
     TRY(dalloc(L, &L->g_sh, (size_t)N * S * as));
@@ -502,26 +515,36 @@ int moe_layer_forward(moe_layer_t* L, void* hidden, void* residual, int32_t n, v
   }
 
   // 2. Shared expert (needs only the normed rows).
+  // MFMA layers: on the side stream, beside fc1, top-k and the sort (small or
+  // latency-bound launches that leave CUs free), joined before the grouped
+  // GEMMs, whose persistent grids would otherwise starve it.
+  const bool side = S > 0 && bf;
+  hipStream_t ss = side ? L->side : s;
+  if (side) {
+    HIP_TRY(hipEventRecord(L->ev_fork, s));
+    HIP_TRY(hipStreamWaitEvent(L->side, L->ev_fork, 0));
+  }
   if (S > 0) {
     {
-      StageScope sc(L, MOE_STAGE_SHARED_UP, s);
+      StageScope sc(L, MOE_STAGE_SHARED_UP, ss);
       GemmArgs a{};
       a.A = L->normed; a.lda = H; a.C = L->g_sh; a.ldc = S;
       a.M = n; a.N = S; a.K = H;
       set_weights(L, a, L->sh_up, L->sh_up_s, L->sh_up_s2, S, H);
-      int rc = gemm(L, a, EPI_RELU2, bf, dc, dgrid, s, "shared up", L->nvfp4);
+      int rc = gemm(L, a, EPI_RELU2, bf, dc, dgrid, ss, "shared up", L->nvfp4);
       if (rc) return rc;
     }
     {
-      StageScope sc(L, MOE_STAGE_SHARED_DOWN, s);
+      StageScope sc(L, MOE_STAGE_SHARED_DOWN, ss);
       GemmArgs b{};
       b.A = L->g_sh; b.lda = S; b.C = L->sh; b.ldc = H;
       b.M = n; b.N = H; b.K = S;
       set_weights(L, b, L->sh_down, L->sh_down_s, L->sh_down_s2, H, S);
-      int rc = gemm(L, b, EPI_STORE, bf, dc, dgrid, s, "shared down", L->nvfp4);
+      int rc = gemm(L, b, EPI_STORE, bf, dc, dgrid, ss, "shared down", L->nvfp4);
       if (rc) return rc;
     }
   }
+  if (side) HIP_TRY(hipEventRecord(L->ev_join, L->side));
 
   // 3. Latent input.
   const void* zin = L->normed;
@@ -550,6 +573,8 @@ int moe_layer_forward(moe_layer_t* L, void* hidden, void* residual, int32_t n, v
   const int tiles_cap = (R + bm - 1) / bm + std::min(E, R);
   // Experts expected to fit one row tile: each weight byte is read once.
   const bool one_tile = (long long)((R + E - 1) / E) * 4 <= (long long)bm * 3;
+
+  if (side) HIP_TRY(hipStreamWaitEvent(s, L->ev_join, 0));
 
   // 5. Grouped expert GEMMs.
   {
