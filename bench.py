@@ -18,7 +18,8 @@ slower of the grouped up / grouped down GEMMs), timed with HIP events on the
 stream it runs on, over the K forwards: in graph mode over an eager pass of
 the same K restored inputs right after the replay (events cannot sit inside
 the graph). The cpu_baseline object times the float64 oracle on a bounded
-token sample of the same workload on the host.
+token sample of the same workload on the host. `layer.ms_per_step_p10_p50_p90`
+is the spread over --replays replays of the same K steps (inputs restored).
 """
 
 from __future__ import annotations
@@ -61,6 +62,9 @@ def main() -> int:
                     help="record every stage (adds event markers to the timed region)")
     ap.add_argument("--eager", action="store_true",
                     help="time K eager forward calls instead of one HIP graph replay of them")
+    ap.add_argument("--replays", type=int, default=5,
+                    help="graph replays of the K steps for the reported spread (the first "
+                         "replay gives value)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -149,6 +153,22 @@ def main() -> int:
     t_wall = time.perf_counter() - t_wall
     ms_total = ev0.elapsed_time(ev1)
     ms_step = ms_total / args.steps
+    # Spread: more replays of the same K steps, each on restored inputs.
+    spread = [ms_step]
+    if graph is not None:
+        for _ in range(args.replays - 1):
+            for j in range(args.warmup, total):
+                inputs[j].copy_(base[j % args.instances])
+            torch.cuda.synchronize()
+            ev0.record(stream)
+            graph.replay()
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            spread.append(ev0.elapsed_time(ev1) / args.steps)
+    spread_sorted = sorted(spread)
+
+    def pct(q):
+        return spread_sorted[min(len(spread_sorted) - 1, int(round(q * (len(spread_sorted) - 1))))]
     if graph is not None:
         # Kernel timing pass (eager, event markers) over the same K inputs,
         # restored first (the forward is in place).
@@ -243,6 +263,9 @@ def main() -> int:
                   "experts_touched": E_t, "max_expert_load": int(max(max_load)),
                   "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
                   "wall_s": round(t_wall, 3),
+                  "ms_per_step_p10_p50_p90": [round(pct(0.1), 4), round(pct(0.5), 4),
+                                              round(pct(0.9), 4)],
+                  "replays": len(spread),
                   "timed": "eager" if args.eager else "graph replay"},
         "cpu_baseline": None,
     }

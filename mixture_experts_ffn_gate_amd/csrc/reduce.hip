@@ -54,10 +54,67 @@ __global__ void __launch_bounds__(256) unpermute_reduce_kernel(
   vec4<T>::st(out + o, acc);
 }
 
+// bf16: one workgroup per token, 8 columns (16 bytes) per thread; the k slot
+// indices and weights are the same for the whole workgroup. Same summation
+// order as above (slots in order, then residual, then shared).
+template <bool LATENT>
+__global__ void __launch_bounds__(1024) unpermute_reduce_bf16_kernel(
+    const bf16* __restrict__ y, const int* __restrict__ inv, const float* __restrict__ w, int k,
+    int D, const bf16* __restrict__ residual, const bf16* __restrict__ sh, bf16* __restrict__ out) {
+  const int t = blockIdx.x;
+  const int d = threadIdx.x * 8;
+  if (d >= D) return;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int p[MOE_MAX_TOPK_REDUCE];
+  float wt[MOE_MAX_TOPK_REDUCE];
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK_REDUCE; ++j)
+    if (j < k) {
+      p[j] = inv[t * k + j];
+      wt[j] = w[t * k + j];
+    }
+  bf16x8 v[MOE_MAX_TOPK_REDUCE];
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK_REDUCE; ++j)
+    if (j < k) v[j] = *(const bf16x8*)(y + (size_t)p[j] * D + d);
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK_REDUCE; ++j)
+    if (j < k)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] += wt[j] * (float)v[j][q];
+  const size_t o = (size_t)t * D + d;
+  if (!LATENT) {
+    const bf16x8 r = *(const bf16x8*)(residual + o);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = (float)r[q] + acc[q];
+    if (sh) {
+      const bf16x8 a = *(const bf16x8*)(sh + o);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] += (float)a[q];
+    }
+  }
+  bf16x8 ob;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) ob[q] = (bf16)acc[q];
+  *(bf16x8*)(out + o) = ob;
+}
+
 hipError_t launch_unpermute_reduce(int dt, bool latent, const void* y, const int* inv,
                                    const float* w, int n, int k, int D, const void* residual,
                                    const void* sh, void* out, hipStream_t s) {
   if (k > MOE_MAX_TOPK_REDUCE) return hipErrorInvalidValue;
+  if (dt == MOE_DT_BF16 && D % 8 == 0 && D / 8 <= 1024) {
+    const dim3 block(((D / 8) + 63) / 64 * 64);
+    if (latent)
+      hipLaunchKernelGGL((unpermute_reduce_bf16_kernel<true>), dim3(n), block, 0, s,
+                         (const bf16*)y, inv, w, k, D, (const bf16*)residual, (const bf16*)sh,
+                         (bf16*)out);
+    else
+      hipLaunchKernelGGL((unpermute_reduce_bf16_kernel<false>), dim3(n), block, 0, s,
+                         (const bf16*)y, inv, w, k, D, (const bf16*)residual, (const bf16*)sh,
+                         (bf16*)out);
+    return hipGetLastError();
+  }
   dim3 grid(n, (D / 4 + 255) / 256);
   if (dt == MOE_DT_BF16) {
     if (latent)
