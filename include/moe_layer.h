@@ -133,8 +133,11 @@ int moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_weights_t* w
  * device-to-host copy. One forward at a time per layer (the workspace is
  * shared). num_tokens == 0 returns MOE_OK with nothing enqueued.
  * Small N (<= 16) runs the weight-streaming GEMV arm; larger N the sorted
- * grouped-GEMM arm. Errors: MOE_ERR_INVALID_ARG, MOE_ERR_TOO_MANY_TOKENS,
- * MOE_ERR_HIP. */
+ * grouped-GEMM arm, whose shared-expert launches go to a layer-owned stream
+ * forked from and joined back to `stream` by events within the call, so all
+ * of the forward's work is ordered after earlier work on `stream` and before
+ * later work on it, and the call captures whole into a HIP graph.
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_TOO_MANY_TOKENS, MOE_ERR_HIP. */
 int moe_layer_forward(moe_layer_t* layer, void* hidden, void* residual, int32_t num_tokens,
                       void* stream);
 

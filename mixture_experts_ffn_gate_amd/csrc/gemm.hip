@@ -12,28 +12,31 @@
 // bf16 MFMA kernel (gemm_mfma_kernel):
 //   * MFMA v_mfma_f32_16x16x32_bf16 with the WEIGHTS as the A operand (16
 //     output features) and the ACTIVATIONS as the B operand (16 tokens), so a
-//     lane's four results are four consecutive output features of one row:
-//     one 8-byte (bf16) or 16-byte (fp32) store.
+//     lane's four results are four consecutive output features of one row.
 //   * Weights are re-tiled once at layer creation into the MFMA lane order:
 //     [N/16][K/32][64 lanes][8], lane l holding feature l%16 and k-elements
 //     8*(l/16)..+7 of its 16x32 block. A wave's weight fetch for one MFMA is
 //     then one contiguous 1 KiB read, and each weight byte is fetched by
 //     exactly one wave (waves own disjoint features).
-//   * A workgroup (4 waves) covers 4*WF features x BMT rows. The BMT x 64
-//     activation slice of each k-step is gathered (rows by the route
+//   * A workgroup (NW = 4 or 8 waves) covers NW*WF features x BMT rows. The
+//     BMT x 64 activation slice of each k-step is gathered (rows by the route
 //     permutation) with 16-byte loads, staged through LDS (double buffered,
 //     XOR-swizzled 16-byte chunks so the MFMA operand reads are conflict-free)
-//     and shared by the 4 waves.
-//   * Weights for step k+1 are in flight while step k computes.
+//     and shared by the waves.
+//   * Weights for step k+1 are in flight while step k computes; the output
+//     tile leaves through LDS as whole rows.
+//   * Persistent grid, XCD-aware tile order (see gemm_mfma_kernel).
 //   * NVFP4 weights (4-bit E2M1 + E4M3 per 16 along K + fp32 scale2 per
 //     matrix; page "metrale_model_arch/nemotron_moe.rs", `ExpertPtrTable`) are
 //     re-tiled the same way and dequantized in registers to exact bf16 before
 //     the MFMA; scale2 multiplies the accumulator in the epilogue.
+//
+// Decode-sized GEMV (gemv_kernel): one workgroup per (row tile of <= 16 rows,
+// 16 features); see below.
 #include <algorithm>
+#include <utility>
 
 #include "kernels.h"
-
-#include <utility>
 
 // ---------------------------------------------------------------------------
 // Tile decode shared by both kernels.
@@ -269,7 +272,7 @@ template <int FT, bool NT> struct WSrc<1, FT, NT> {
 // two at any tile height here, and cost occupancy at 64-row tiles.
 constexpr int mfma_stages(int) { return 2; }
 
-// One output tile: BMT rows x (4 waves x WF) features.
+// One output tile: BMT rows x (NW waves x WF) features.
 template <int WF, int BMT, int NW, int EPI, typename TC, int WQ, bool GROUPED, bool NT>
 __device__ __forceinline__ void mfma_tile(const GemmArgs& a, int slot, int ftile,
                                           bf16* __restrict__ xs) {
@@ -591,9 +594,6 @@ hipError_t launch_gemm_mfma(const GemmArgs& a, MfmaCfg cfg, int epi, bool tc_bf1
 // MFMA registers), so many loads are in flight per CU even for one token.
 // The partial sums meet in LDS and are added in wave order (deterministic).
 // ---------------------------------------------------------------------------
-#ifndef MOE_GEMV_GU
-#define MOE_GEMV_GU 4
-#endif
 struct GemvArgs {
   GemmArgs seg[2];
   int nseg;
@@ -603,7 +603,7 @@ struct GemvArgs {
 
 template <int EPI, typename TC, int WQ>
 __global__ void __launch_bounds__(256) gemv_kernel(GemvArgs g) {
-  constexpr int GU = MOE_GEMV_GU;  // k-steps per load group
+  constexpr int GU = 4;  // k-steps per load group (6 and 8 measured no faster)
   using Src = WSrc<WQ, 1, true>;
   using Frag = typename Src::Frag;
   __shared__ floatx4 part[3][64];

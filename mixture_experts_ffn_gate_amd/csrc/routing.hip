@@ -1,8 +1,14 @@
 // Routing front end of the MoE layer on gfx950:
-//   norm_gate_kernel   RMSNorm (+ residual save) fused with the gate projection
-//   topk_sigmoid_kernel  wave64 sigmoid top-k with renormalized weights
-//   route_sort_kernel  per-expert histogram, prefix sum and stable scatter,
-//                      plus the (expert, row-block) tile list of the grouped GEMMs
+//   norm_gate_lds_kernel   bf16: RMSNorm (+ residual save) fused with the gate
+//                          projection on MFMA, token rows staged in LDS
+//   norm_gate_mfma_kernel  bf16, H too large for the LDS staging
+//   norm_gate_kernel       fp32 layers (SIMT)
+//   topk_sigmoid_kernel    wave64 sigmoid top-k with renormalized weights
+//   route_sort_kernel      per-expert histogram, prefix sum and stable scatter,
+//                          plus the (expert, row-block) tile list of the
+//                          grouped GEMMs (one workgroup; route_hist_kernel +
+//                          route_scatter_kernel when R exceeds one chunk)
+//   route_small_kernel     decode-sized batches: all of the above in one launch
 //
 // Sources: page "metrale_model_arch/nemotron_moe.rs" (module doc: forward
 // order RMS norm -> gate -> sigmoid top-k; `prefill`: rms_norm_residual,
