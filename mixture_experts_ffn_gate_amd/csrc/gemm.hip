@@ -268,15 +268,29 @@ template <int FT, bool NT> struct WSrc<1, FT, NT> {
 // ---------------------------------------------------------------------------
 // Persistent MFMA GEMM (grouped or dense), WQ = 0 bf16 weights, 1 NVFP4.
 // ---------------------------------------------------------------------------
-// Pipeline depth (k-steps in flight). Three stages measured no faster than
-// two at any tile height here, and cost occupancy at 64-row tiles.
-constexpr int mfma_stages(int) { return 2; }
+// Pipeline depth S: the loads of step k+S-1 are issued at the start of step
+// k, and a gathered activation slice waits one more step in registers before
+// it goes to LDS.
+// Measured on the layer's shapes: three stages pay on 128 x 256 tiles (7-9%
+// on the grouped GEMMs from 4096 tokens up, 2% on the latent layer) and on
+// DEEP launches (dense, at most one 128 x 128 tile per CU, so one resident
+// workgroup per CU and the register budget of a whole SIMD: 8-10% on the
+// shared expert at 1024 tokens); two elsewhere (three cost 2-5% on 64-row
+// tiles, and spill at two 128 x 128 workgroups per CU).
+constexpr int mfma_stages(int bmt, int nw, int wq, bool deep) {
+  return deep || (bmt == 128 && nw == 8 && wq == 0) ? 3 : 2;
+}
+// Workgroups per CU the register budget is sized for.
+constexpr int mfma_min_blocks(int bmt, int nw, bool deep) {
+  return (bmt >= 128 && nw == 4 && !deep) ? 2 : 1;
+}
 
 // One output tile: BMT rows x (NW waves x WF) features.
-template <int WF, int BMT, int NW, int EPI, typename TC, int WQ, bool GROUPED, bool NT>
+template <int WF, int BMT, int NW, int EPI, typename TC, int WQ, bool GROUPED, bool NT,
+          bool DEEP>
 __device__ __forceinline__ void mfma_tile(const GemmArgs& a, int slot, int ftile,
                                           bf16* __restrict__ xs) {
-  constexpr int S = mfma_stages(BMT);
+  constexpr int S = mfma_stages(BMT, NW, WQ, DEEP);
   constexpr int FT = WF / 16;      // 16-feature tiles per wave
   constexpr int TT = BMT / 16;     // 16-row tiles per workgroup
   constexpr int BK = 64;           // k per step (two MFMA k-chunks of 32)
@@ -321,22 +335,25 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs& a, int slot, int ftile
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) acc[ft][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // S-stage pipeline: the weights of step k+S-1 are loaded (into register set
-  // (k+S-1)%S) while step k computes, so S-1 steps of compute cover their
-  // latency; the activations of step k+S-1 are loaded at the start of step k
-  // and written to LDS slot (k+S-1)%S (consumed at step k-1) after its MFMAs.
-  // The ring index is a compile-time constant: the k-loop is unrolled by S.
+  // S-stage pipeline. At the start of step k the weights and the activation
+  // slice of step k+S-1 are loaded into register set (k+S-1)%S. After the
+  // MFMAs of step k, the slice of step k+1 (loaded at step k+2-S) goes from
+  // its registers into LDS slot (k+1)%S. With S >= 3 a gathered slice is thus
+  // written to LDS one step after its load was issued, and its latency hides
+  // under two steps of MFMAs instead of one; with S = 2 the slice is loaded
+  // and stored in the same step. The ring index is a compile-time constant:
+  // the k-loop is unrolled by S.
   Frag w[S];
-  bf16x8 areg[LPASS];
+  bf16x8 areg[S][LPASS];
 #pragma unroll
   for (int p = 0; p < S - 1; ++p) {
     const int kp = min(p, nsteps - 1);
     src.load(w[p], kp);
 #pragma unroll
-    for (int i = 0; i < LPASS; ++i) areg[i] = *(const bf16x8*)(asrc[i] + kp * BK);
-#pragma unroll
-    for (int i = 0; i < LPASS; ++i) *(bf16x8*)(&xs[p * BMT * 64 + lds_off[i]]) = areg[i];
+    for (int i = 0; i < LPASS; ++i) areg[p][i] = *(const bf16x8*)(asrc[i] + kp * BK);
   }
+#pragma unroll
+  for (int i = 0; i < LPASS; ++i) *(bf16x8*)(&xs[lds_off[i]]) = areg[0][i];
   __syncthreads();
 
   const int brow = lane & 15, bch = lane >> 4;
@@ -359,31 +376,33 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs& a, int slot, int ftile
       }
     }
   };
-  // Step k (ring slot u = k % S). PREF: whether step k+S-1 exists (the steady
-  // state always prefetches; only the last S-1 steps of an item skip it).
-  auto step = [&](int k, auto u_c, bool pref) {
+  // Step k (ring slot u = k % S). PREF: whether step k+S-1 exists; STAGE:
+  // whether step k+1 exists (the steady state does both; only the last steps
+  // of an item skip them).
+  auto step = [&](int k, auto u_c, bool pref, bool stage) {
     constexpr int u = decltype(u_c)::value;
-    constexpr int un = (u + S - 1) % S;
+    constexpr int un = (u + S - 1) % S;  // ring slot of step k+S-1
+    constexpr int u1 = (u + 1) % S;      // ring slot of step k+1
     const int kn = k + S - 1;
     if (pref) {
 #pragma unroll
-      for (int i = 0; i < LPASS; ++i) areg[i] = *(const bf16x8*)(asrc[i] + kn * BK);
+      for (int i = 0; i < LPASS; ++i) areg[un][i] = *(const bf16x8*)(asrc[i] + kn * BK);
       src.load(w[un], kn);
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
     compute(u, w[u]);
-    if (pref) {
+    if (stage) {
 #pragma unroll
-      for (int i = 0; i < LPASS; ++i) *(bf16x8*)(&xs[un * BMT * 64 + lds_off[i]]) = areg[i];
+      for (int i = 0; i < LPASS; ++i) *(bf16x8*)(&xs[u1 * BMT * 64 + lds_off[i]]) = areg[u1][i];
     }
     __syncthreads();
   };
   auto group = [&](int k0, bool tail) {
     [&]<int... U>(std::integer_sequence<int, U...>) {
       ((tail ? (k0 + U < nsteps ? step(k0 + U, std::integral_constant<int, U>{},
-                                       k0 + U + S - 1 < nsteps)
+                                       k0 + U + S - 1 < nsteps, k0 + U + 1 < nsteps)
                                 : void())
-             : step(k0 + U, std::integral_constant<int, U>{}, true)),
+             : step(k0 + U, std::integral_constant<int, U>{}, true, true)),
        ...);
     }(std::make_integer_sequence<int, S>{});
   };
@@ -458,15 +477,16 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs& a, int slot, int ftile
 }
 
 // LDS of one workgroup: the activation stages, or the staged output tile.
-constexpr int mfma_lds_elems(int bmt, int cw) {
-  return mfma_stages(bmt) * bmt * 64 > bmt * (cw + 8) ? mfma_stages(bmt) * bmt * 64
-                                                      : bmt * (cw + 8);
+constexpr int mfma_lds_elems(int stages, int bmt, int cw) {
+  return stages * bmt * 64 > bmt * (cw + 8) ? stages * bmt * 64 : bmt * (cw + 8);
 }
 
-template <int WF, int BMT, int NW, int EPI, typename TC, int WQ, bool GROUPED, bool NT>
-__global__ void __launch_bounds__(NW * 64, (BMT >= 128 && NW == 4 ? 2 : 1))
+template <int WF, int BMT, int NW, int EPI, typename TC, int WQ, bool GROUPED, bool NT,
+          bool DEEP>
+__global__ void __launch_bounds__(NW * 64, mfma_min_blocks(BMT, NW, DEEP))
     gemm_mfma_kernel(GemmArgs a, int nft, int slots, int wg_per_xcd, int rows_major) {
-  __shared__ __attribute__((aligned(16))) bf16 xs[mfma_lds_elems(BMT, NW * WF)];
+  __shared__ __attribute__((aligned(16)))
+  bf16 xs[mfma_lds_elems(mfma_stages(BMT, NW, WQ, DEEP), BMT, NW * WF)];
   const int xcd = blockIdx.x & 7;
   const int live = GROUPED ? min(*a.num_tiles, slots) : slots;
   const int outer = rows_major ? live : nft;    // the axis split over the XCDs
@@ -489,17 +509,18 @@ __global__ void __launch_bounds__(NW * 64, (BMT >= 128 && NW == 4 ? 2 : 1))
       slot = item % inner;
       ftile = o0 + item / inner;
     }
-    mfma_tile<WF, BMT, NW, EPI, TC, WQ, GROUPED, NT>(a, slot, ftile, xs);
+    mfma_tile<WF, BMT, NW, EPI, TC, WQ, GROUPED, NT, DEEP>(a, slot, ftile, xs);
   }
 }
 
-template <int WF, int BMT, int NW, int EPI, typename TC, int WQ, bool GROUPED, bool NT>
+template <int WF, int BMT, int NW, int EPI, typename TC, int WQ, bool GROUPED, bool NT,
+          bool DEEP>
 static hipError_t launch_persistent(const GemmArgs& a, int slots, hipStream_t s) {
   static int occ = 0;  // resident workgroups per CU (queried once per process)
   if (occ == 0) {
     int o = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &o, (const void*)gemm_mfma_kernel<WF, BMT, NW, EPI, TC, WQ, GROUPED, NT>, NW * 64,
+            &o, (const void*)gemm_mfma_kernel<WF, BMT, NW, EPI, TC, WQ, GROUPED, NT, DEEP>, NW * 64,
             0) !=
             hipSuccess ||
         o < 1)
@@ -523,27 +544,30 @@ static hipError_t launch_persistent(const GemmArgs& a, int slots, hipStream_t s)
   const int outer = rows_major ? slots : nft, inner = rows_major ? nft : slots;
   const int max_items_per_xcd = ((outer + 7) / 8) * inner;
   const int wg_per_xcd = std::max(1, std::min(max_items_per_xcd, (cus / 8) * occ));
-  hipLaunchKernelGGL((gemm_mfma_kernel<WF, BMT, NW, EPI, TC, WQ, GROUPED, NT>),
+  hipLaunchKernelGGL((gemm_mfma_kernel<WF, BMT, NW, EPI, TC, WQ, GROUPED, NT, DEEP>),
                      dim3(8 * wg_per_xcd), dim3(NW * 64), 0, s, a, nft, slots, wg_per_xcd,
                      rows_major);
   return hipGetLastError();
 }
 
-template <int WF, int BMT, int NW, int WQ, bool G, bool NT>
+template <int WF, int BMT, int NW, int WQ, bool G, bool NT, bool DEEP = false>
 static hipError_t launch_mfma_shape(const GemmArgs& a, int epi, int slots, hipStream_t s) {
   switch (epi) {
-    case EPI_RELU2: return launch_persistent<WF, BMT, NW, EPI_RELU2, bf16, WQ, G, NT>(a, slots, s);
-    case EPI_STORE: return launch_persistent<WF, BMT, NW, EPI_STORE, bf16, WQ, G, NT>(a, slots, s);
+    case EPI_RELU2:
+      return launch_persistent<WF, BMT, NW, EPI_RELU2, bf16, WQ, G, NT, DEEP>(a, slots, s);
+    case EPI_STORE:
+      return launch_persistent<WF, BMT, NW, EPI_STORE, bf16, WQ, G, NT, DEEP>(a, slots, s);
     case EPI_ADD_RES:  // only the dense fc2 adds residual + shared
       if (G) return hipErrorInvalidValue;
-      return launch_persistent<WF, BMT, NW, EPI_ADD_RES, bf16, WQ, false, NT>(a, slots, s);
+      return launch_persistent<WF, BMT, NW, EPI_ADD_RES, bf16, WQ, false, NT, DEEP>(a, slots, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 // bf16 128-row tiles take 8 waves (128 x 256 outputs per workgroup: a
 // quarter less L1 traffic per MFMA) when that still gives every CU two tiles
-// or more; smaller launches keep 4 waves so that more CUs get work. NVFP4
+// or more; smaller launches keep 4 waves so that more CUs get work, and dense
+// ones with at most one 4-wave tile per CU take the DEEP variant. NVFP4
 // weights bring a quarter of the bytes, and measured faster with 4 waves.
 template <int WQ, bool G, bool NT>
 static hipError_t launch_mfma_wq(const GemmArgs& a, MfmaCfg cfg, int epi, int slots,
@@ -558,8 +582,13 @@ static hipError_t launch_mfma_wq(const GemmArgs& a, MfmaCfg cfg, int epi, int sl
       cus = n;
     }
     const long long items8 = (long long)slots * ((a.N + 255) / 256);
+    const long long items4 = (long long)slots * ((a.N + 127) / 128);
     if (WQ == 0 && items8 >= 2LL * cus)
       return launch_mfma_shape<32, 128, 8, WQ, G, NT>(a, epi, slots, s);
+    // A dense bf16 launch with at most one tile per CU runs one workgroup per
+    // CU with a deeper pipeline.
+    if constexpr (WQ == 0 && !G)
+      if (items4 <= cus) return launch_mfma_shape<32, 128, 4, WQ, G, NT, true>(a, epi, slots, s);
     return launch_mfma_shape<32, 128, 4, WQ, G, NT>(a, epi, slots, s);
   }
 #define SHAPE(W, M) \

@@ -576,21 +576,31 @@ __global__ void __launch_bounds__(1024) route_scatter_kernel(
 // ---------------------------------------------------------------------------
 // RMSNorm + gate for bf16 layers with the token rows staged in LDS.
 // Block = 8 waves, 16 tokens x ET expert tiles of 16.
+//   0. Each wave issues the loads of its first batch of gate fragments at
+//      entry: they do not depend on the rows, so their latency overlaps the
+//      row loads.
 //   1. The 16 hidden rows are read once with contiguous 16-byte loads into
 //      LDS (row stride H + 8 elements: the 16 rows of an MFMA operand read
-//      fall in distinct banks); the residual copy is written on the way and
-//      each wave sums the squares of its rows. gamma is staged as well.
+//      fall in distinct banks); each wave issues the loads of both its rows
+//      before it uses any, and sums the squares of its rows. gamma is staged
+//      as well.
 //   2. Wave w takes expert tile w % ET and the k-steps {j : j % (8/ET) ==
 //      w / ET} of it. The A operand (gate rows) comes from the pre-tiled gate
-//      matrix [E16/16][H/32][64 lanes][8] (one contiguous 1 KiB per wave load);
-//      the B operand is built from LDS: n = x * rinv * gamma in fp32, split
-//      into hi = bf16(n) and lo = bf16(n - hi), two MFMAs per step, so the
-//      logits see ~16 mantissa bits of the fp32 normed value.
-//   3. Partial sums of a tile meet in LDS and are added in fixed order.
-//   Blocks with blockIdx.y == 0 also write normed = bf16(n) from LDS.
+//      matrix [E16/16][H/32][64 lanes][8] (one contiguous 1 KiB per wave load),
+//      in batches of NG_U steps, the next batch in flight while one computes;
+//      the B operand is built from LDS: y = x * gamma, exact in fp32 (two
+//      8-bit mantissas), split into hi = bf16(y) and lo = bf16(y - hi), two
+//      MFMAs per step, so the dot products see y to ~16 bits.
+//   3. Partial sums of a tile meet in LDS and are added in fixed order, then
+//      scaled by the row's fp32 inverse RMS: logit = rinv * (W_g . y), the
+//      gate of the fp32 normed row.
+//   The residual copy and normed = bf16(n) are written by all blocks of a
+//   token group, each taking one contiguous range of 16-byte column chunks.
 // ---------------------------------------------------------------------------
 // LDS of one block: 16 rows of H + 8, gamma, partial sums, 16 inverse RMS.
 constexpr size_t NG_LDS_MAX = 160 * 1024;
+constexpr int NG_U = 8;   // gate k-steps per load batch
+constexpr int NG_NB = 8;  // 16-byte chunks per lane and row in one load round
 
 template <int ET>
 __global__ void __launch_bounds__(512) norm_gate_lds_kernel(const bf16* __restrict__ hidden,
@@ -609,62 +619,78 @@ __global__ void __launch_bounds__(512) norm_gate_lds_kernel(const bf16* __restri
   float* rinv = (float*)(red + 8 * 64);             // [16]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * 16;
-  const bool writer = blockIdx.y == 0;
+  // this block's share of the 16-byte column chunks for the residual and normed copies
+  const int nch = H >> 3;
+  const int c_lo = blockIdx.y * nch / gridDim.y, c_hi = (blockIdx.y + 1) * nch / gridDim.y;
 
-  // 1. rows -> LDS (wave w: rows 2w, 2w+1), residual copy, sums of squares
-  for (int i = tid * 8; i < H; i += 512 * 8) *(bf16x8*)(gs + i) = *(const bf16x8*)(gamma + i);
-#pragma unroll
-  for (int rr = 0; rr < 2; ++rr) {
-    const int r = wave * 2 + rr;
-    const bool valid = t0 + r < n;
-    const bf16* x = hidden + (size_t)min(t0 + r, n - 1) * H;
-    float ss = 0.f;
-    for (int i0 = lane * 8; i0 < H; i0 += 64 * 8 * 4) {
-      bf16x8 v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = i0 + u * 512;
-        v[u] = i < H ? *(const bf16x8*)(x + i) : bf16x8{};
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = i0 + u * 512;
-        if (i < H) {
-          *(bf16x8*)(xs + r * HP + i) = v[u];
-          if (writer && valid) *(bf16x8*)(residual + (size_t)(t0 + r) * H + i) = v[u];
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const float f = (float)v[u][q];
-            ss += f * f;
-          }
-        }
-      }
-    }
-    ss = wave_sum(ss);
-    if (lane == 0) rinv[r] = 1.0f / sqrtf(ss / (float)H + eps);
-  }
-  __syncthreads();
-
-  // 2. gate: expert tile et = e0/16 + wave % ET, k-steps j = ks, ks + KS, ...
-  const int tok = lane & 15, kg = lane >> 4;
-  const float rv = rinv[tok];
+  // 0. first batch of gate fragments: expert tile et, k-steps ks, ks + KS, ...
   const int et = wave % ET, ks = wave / ET;
   const int tile = blockIdx.y * ET + et;
   const int nsteps = H / 32;
   const bf16* wt = wgate_t + ((size_t)tile * nsteps * 64 + lane) * 8;
-  const bf16* xrow = xs + tok * HP + kg * 8;
-  const bf16* grow = gs + kg * 8;
-  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-  constexpr int U = 8;
-  for (int j0 = ks; j0 < nsteps; j0 += KS * U) {
-    bf16x8 wf[U];
+  auto load_batch = [&](bf16x8 (&wf)[NG_U], int j0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < NG_U; ++u) {
       const int j = min(j0 + u * KS, nsteps - 1);  // past the end: a valid step, not used
       wf[u] = *(const bf16x8*)(wt + (size_t)j * 512);
     }
+  };
+  bf16x8 wa[NG_U], wb[NG_U];
+  load_batch(wa, ks);
+
+  // 1. gamma and rows -> LDS (wave w: rows 2w, 2w+1), residual copy, sums of squares
+  for (int i = tid * 8; i < H; i += 512 * 8) *(bf16x8*)(gs + i) = *(const bf16x8*)(gamma + i);
+  {
+    const int r0 = wave * 2;
+    const bool valid0 = t0 + r0 < n, valid1 = t0 + r0 + 1 < n;
+    const bf16* x0 = hidden + (size_t)min(t0 + r0, n - 1) * H;
+    const bf16* x1 = hidden + (size_t)min(t0 + r0 + 1, n - 1) * H;
+    float ss0 = 0.f, ss1 = 0.f;
+    for (int i0 = lane * 8; i0 < H; i0 += 512 * NG_NB) {
+      bf16x8 v0[NG_NB], v1[NG_NB];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < NG_NB; ++u) {
+        const int i = i0 + u * 512;
+        v0[u] = i < H ? *(const bf16x8*)(x0 + i) : bf16x8{};
+        v1[u] = i < H ? *(const bf16x8*)(x1 + i) : bf16x8{};
+      }
+#pragma unroll
+      for (int u = 0; u < NG_NB; ++u) {
+        const int i = i0 + u * 512;
+        if (i < H) {
+          *(bf16x8*)(xs + r0 * HP + i) = v0[u];
+          *(bf16x8*)(xs + (r0 + 1) * HP + i) = v1[u];
+          if ((i >> 3) >= c_lo && (i >> 3) < c_hi) {
+            if (valid0) *(bf16x8*)(residual + (size_t)(t0 + r0) * H + i) = v0[u];
+            if (valid1) *(bf16x8*)(residual + (size_t)(t0 + r0 + 1) * H + i) = v1[u];
+          }
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const float f0 = (float)v0[u][q], f1 = (float)v1[u][q];
+            ss0 += f0 * f0;
+            ss1 += f1 * f1;
+          }
+        }
+      }
+    }
+    ss0 = wave_sum(ss0);
+    ss1 = wave_sum(ss1);
+    if (lane == 0) {
+      rinv[r0] = 1.0f / sqrtf(ss0 / (float)H + eps);
+      rinv[r0 + 1] = 1.0f / sqrtf(ss1 / (float)H + eps);
+    }
+  }
+  __syncthreads();
+
+  // 2. gate: batches of NG_U k-steps, the next batch loading while one computes
+  const int tok = lane & 15, kg = lane >> 4;
+  const float rv = rinv[tok];
+  const bf16* xrow = xs + tok * HP + kg * 8;
+  const bf16* grow = gs + kg * 8;
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto compute_batch = [&](const bf16x8 (&wf)[NG_U], int j0) {
+#pragma unroll
+    for (int u = 0; u < NG_U; ++u) {
       const int j = j0 + u * KS;
       if (j >= nsteps) break;
       const bf16x8 xv = *(const bf16x8*)(xrow + j * 32);
@@ -672,31 +698,38 @@ __global__ void __launch_bounds__(512) norm_gate_lds_kernel(const bf16* __restri
       bf16x8 hi, lo;
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        const float v = (float)xv[q] * rv * (float)gv[q];
+        const float v = (float)xv[q] * (float)gv[q];  // exact: 8-bit x 8-bit mantissas
         hi[q] = (bf16)v;
         lo[q] = (bf16)(v - (float)hi[q]);
       }
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u], hi, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u], lo, acc, 0, 0, 0);
     }
+  };
+  constexpr int BS = KS * NG_U;  // k-steps between consecutive batches of a wave
+  for (int j0 = ks; j0 < nsteps; j0 += 2 * BS) {
+    if (j0 + BS < nsteps) load_batch(wb, j0 + BS);
+    compute_batch(wa, j0);
+    if (j0 + BS >= nsteps) break;
+    if (j0 + 2 * BS < nsteps) load_batch(wa, j0 + 2 * BS);
+    compute_batch(wb, j0 + BS);
   }
   red[wave * 64 + lane] = acc;
 
-  // normed rows (writer blocks): wave w rows 2w, 2w+1, from LDS
-  if (writer) {
+  // normed rows: wave w rows 2w, 2w+1, this block's column chunks, from LDS
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const int r = wave * 2 + rr;
-      if (t0 + r >= n) continue;
-      const float rr_inv = rinv[r];
-      for (int i = lane * 8; i < H; i += 512) {
-        const bf16x8 xv = *(const bf16x8*)(xs + r * HP + i);
-        const bf16x8 gv = *(const bf16x8*)(gs + i);
-        bf16x8 o;
+  for (int rr = 0; rr < 2; ++rr) {
+    const int r = wave * 2 + rr;
+    if (t0 + r >= n) continue;
+    const float rr_inv = rinv[r];
+    for (int i = lane * 8; i < H; i += 512) {
+      if ((i >> 3) < c_lo || (i >> 3) >= c_hi) continue;
+      const bf16x8 xv = *(const bf16x8*)(xs + r * HP + i);
+      const bf16x8 gv = *(const bf16x8*)(gs + i);
+      bf16x8 o;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) o[q] = (bf16)((float)xv[q] * rr_inv * (float)gv[q]);
-        *(bf16x8*)(normed + (size_t)(t0 + r) * H + i) = o;
-      }
+      for (int q = 0; q < 8; ++q) o[q] = (bf16)((float)xv[q] * rr_inv * (float)gv[q]);
+      *(bf16x8*)(normed + (size_t)(t0 + r) * H + i) = o;
     }
   }
   __syncthreads();
@@ -706,6 +739,7 @@ __global__ void __launch_bounds__(512) norm_gate_lds_kernel(const bf16* __restri
     floatx4 v = red[wave * 64 + lane];
 #pragma unroll
     for (int k2 = 1; k2 < KS; ++k2) v += red[(wave + k2 * ET) * 64 + lane];
+    v *= rv;  // the row's inverse RMS, in fp32
     const int e = (blockIdx.y * ET + wave) * 16 + 4 * kg;
     if (t0 + tok < n && e < E) {
       float* dst = logits + (size_t)(t0 + tok) * E + e;
