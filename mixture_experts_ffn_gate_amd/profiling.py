@@ -35,11 +35,12 @@ def source_hash() -> str:
 
 
 _MANGLED = re.compile(
-    r"gemm_mfma_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E\w+?Li(\d+)ELb(\d)E(?:Lb(\d)E)?")
+    r"gemm_mfma_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E\w+?Li(\d+)ELb(\d)E(?:Lb(\d)E)?(?:Lb(\d)E)?")
 # The profiler's demangler renders the bf16 argument as "bool _Accum" and an
 # NVFP4 weight flag as "int, E"; it leaves the bf16-weight kernels mangled.
 _DEMANGLED = re.compile(
-    r"gemm_mfma_kernel<(\d+), (\d+), (\d+), (\d+), (.*?), (true|false)(?:, (true|false))?>")
+    r"gemm_mfma_kernel<(\d+), (\d+), (\d+), (\d+), (.*?), (true|false)(?:, (true|false))?"
+    r"(?:, (true|false))?>")
 _GEMV_MANGLED = re.compile(r"gemv_kernelILi(\d+)E\w+?Li(\d+)EE()")
 _GEMV_DEMANGLED = re.compile(r"gemv_kernel<(\d+), (.*)>()")
 _EPI = {"0": "relu2", "1": "store", "2": "add_res"}
@@ -53,15 +54,16 @@ def short_name(name: str) -> str:
     """Readable kernel label; GEMMs by role (grouped/dense, epilogue, weights, tile)."""
     m = _MANGLED.search(name)
     if m:
-        wf, bmt, nw, epi, wq, g, nt = m.groups()
+        wf, bmt, nw, epi, wq, g, nt, deep = m.groups()
         return (f"gemm[{'grouped' if g == '1' else 'dense'},{_EPI.get(epi, epi)},"
                 f"{'nvfp4' if wq == '1' else 'bf16'},{int(wf) * int(nw)}x{bmt}"
-                f"{',nt' if nt == '1' else ''}]")
+                f"{',nt' if nt == '1' else ''}{',deep' if deep == '1' else ''}]")
     m = _DEMANGLED.search(name)
     if m:
-        wf, bmt, nw, epi, mid, g, nt = m.groups()
+        wf, bmt, nw, epi, mid, g, nt, deep = m.groups()
         return (f"gemm[{'grouped' if g == 'true' else 'dense'},{_EPI.get(epi, epi)},"
-                f"{_wq(mid)},{int(wf) * int(nw)}x{bmt}{',nt' if nt == 'true' else ''}]")
+                f"{_wq(mid)},{int(wf) * int(nw)}x{bmt}{',nt' if nt == 'true' else ''}"
+                f"{',deep' if deep == 'true' else ''}]")
     m = _GEMV_MANGLED.search(name)
     if m:
         epi, wq, norm = m.groups()

@@ -97,6 +97,15 @@ def test_profile_kernel_labels():
         == "gemm[dense,relu2,bf16,256x128]"
     assert short_name("void gemm_mfma_kernel<32, 128, 4, 0, bool _Accum, int, E, true, false>"
                       "(GemmArgs, int, int, int, int)") == "gemm[grouped,relu2,nvfp4,128x128]"
+    # current symbols carry a third flag (the deep-pipeline dense variant)
+    assert short_name("_Z16gemm_mfma_kernelILi32ELi64ELi4ELi1EDF16bLi0ELb1ELb1ELb0EEv8GemmArgsiiii") \
+        == "gemm[grouped,store,bf16,128x64,nt]"
+    assert short_name("_Z16gemm_mfma_kernelILi32ELi128ELi4ELi0EDF16bLi0ELb0ELb0ELb1EEv8GemmArgsiiii") \
+        == "gemm[dense,relu2,bf16,128x128,deep]"
+    assert short_name("void gemm_mfma_kernel<32, 128, 4, 0, bool _Accum, int, E, true, false, false>"
+                      "(GemmArgs, int, int, int, int)") == "gemm[grouped,relu2,nvfp4,128x128]"
+    assert short_name("void gemm_mfma_kernel<32, 128, 4, 1, bool _Accum, int, E, false, false, false>"
+                      "(GemmArgs, int, int, int, int)") == "gemm[dense,store,nvfp4,128x128]"
     assert short_name("_Z11gemv_kernelILi1EDF16bLi0EEv8GemvArgs") == "gemv[store,bf16]"
     assert short_name("_Z11gemv_kernelILi1EDF16bLi1EEv8GemvArgs") == "gemv[store,nvfp4]"
     assert short_name("void route_small_kernel<2>(bool _Accum const*)") == "route_small"
