@@ -272,13 +272,14 @@ template <int FT, bool NT> struct WSrc<1, FT, NT> {
 // k, and a gathered activation slice waits one more step in registers before
 // it goes to LDS.
 // Measured on the layer's shapes: three stages pay on 128 x 256 tiles (7-9%
-// on the grouped GEMMs from 4096 tokens up, 2% on the latent layer) and on
+// on the bf16 grouped GEMMs from 4096 tokens up, 2% on the latent layer, 1%
+// on NVFP4 weights at 4096 tokens) and on
 // DEEP launches (dense, at most one 128 x 128 tile per CU, so one resident
 // workgroup per CU and the register budget of a whole SIMD: 8-10% on the
 // shared expert at 1024 tokens); two elsewhere (three cost 2-5% on 64-row
 // tiles, and spill at two 128 x 128 workgroups per CU).
-constexpr int mfma_stages(int bmt, int nw, int wq, bool deep) {
-  return deep || (bmt == 128 && nw == 8 && wq == 0) ? 3 : 2;
+constexpr int mfma_stages(int bmt, int nw, bool deep) {
+  return deep || (bmt == 128 && nw == 8) ? 3 : 2;
 }
 // Workgroups per CU the register budget is sized for.
 constexpr int mfma_min_blocks(int bmt, int nw, bool deep) {
@@ -290,7 +291,7 @@ template <int WF, int BMT, int NW, int EPI, typename TC, int WQ, bool GROUPED, b
           bool DEEP>
 __device__ __forceinline__ void mfma_tile(const GemmArgs& a, int slot, int ftile,
                                           bf16* __restrict__ xs) {
-  constexpr int S = mfma_stages(BMT, NW, WQ, DEEP);
+  constexpr int S = mfma_stages(BMT, NW, DEEP);
   constexpr int FT = WF / 16;      // 16-feature tiles per wave
   constexpr int TT = BMT / 16;     // 16-row tiles per workgroup
   constexpr int BK = 64;           // k per step (two MFMA k-chunks of 32)
@@ -486,7 +487,7 @@ template <int WF, int BMT, int NW, int EPI, typename TC, int WQ, bool GROUPED, b
 __global__ void __launch_bounds__(NW * 64, mfma_min_blocks(BMT, NW, DEEP))
     gemm_mfma_kernel(GemmArgs a, int nft, int slots, int wg_per_xcd, int rows_major) {
   __shared__ __attribute__((aligned(16)))
-  bf16 xs[mfma_lds_elems(mfma_stages(BMT, NW, WQ, DEEP), BMT, NW * WF)];
+  bf16 xs[mfma_lds_elems(mfma_stages(BMT, NW, DEEP), BMT, NW * WF)];
   const int xcd = blockIdx.x & 7;
   const int live = GROUPED ? min(*a.num_tiles, slots) : slots;
   const int outer = rows_major ? live : nft;    // the axis split over the XCDs
@@ -564,11 +565,10 @@ static hipError_t launch_mfma_shape(const GemmArgs& a, int epi, int slots, hipSt
   }
 }
 
-// bf16 128-row tiles take 8 waves (128 x 256 outputs per workgroup: a
-// quarter less L1 traffic per MFMA) when that still gives every CU two tiles
-// or more; smaller launches keep 4 waves so that more CUs get work, and dense
-// ones with at most one 4-wave tile per CU take the DEEP variant. NVFP4
-// weights bring a quarter of the bytes, and measured faster with 4 waves.
+// 128-row tiles take 8 waves (128 x 256 outputs per workgroup: a quarter
+// less L1 traffic per MFMA) when that still gives every CU two tiles or more;
+// smaller launches keep 4 waves so that more CUs get work, and dense bf16 ones
+// with at most one 4-wave tile per CU take the DEEP variant.
 template <int WQ, bool G, bool NT>
 static hipError_t launch_mfma_wq(const GemmArgs& a, MfmaCfg cfg, int epi, int slots,
                                  hipStream_t s) {
@@ -583,7 +583,7 @@ static hipError_t launch_mfma_wq(const GemmArgs& a, MfmaCfg cfg, int epi, int sl
     }
     const long long items8 = (long long)slots * ((a.N + 255) / 256);
     const long long items4 = (long long)slots * ((a.N + 127) / 128);
-    if (WQ == 0 && items8 >= 2LL * cus)
+    if (items8 >= 2LL * cus)
       return launch_mfma_shape<32, 128, 8, WQ, G, NT>(a, epi, slots, s);
     // A dense bf16 launch with at most one tile per CU runs one workgroup per
     // CU with a deeper pipeline.
