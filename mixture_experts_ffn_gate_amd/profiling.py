@@ -23,7 +23,10 @@ import re
 from collections import defaultdict
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ("csrc/gemm.hip", "csrc/routing.hip", "csrc/reduce.hip", "csrc/layer.cpp")
+# The kernel and launch sources, and the build script (its compiler flags
+# change the generated kernels too).
+KERNEL_SOURCES = ("csrc/gemm.hip", "csrc/routing.hip", "csrc/reduce.hip", "csrc/layer.cpp",
+                  "build.py")
 
 
 def source_hash() -> str:
