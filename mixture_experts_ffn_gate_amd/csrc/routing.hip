@@ -584,23 +584,31 @@ __global__ void __launch_bounds__(1024) route_scatter_kernel(
 //      fall in distinct banks); each wave issues the loads of both its rows
 //      before it uses any, and sums the squares of its rows. gamma is staged
 //      as well.
-//   2. Wave w takes expert tile w % ET and the k-steps {j : j % (8/ET) ==
-//      w / ET} of it. The A operand (gate rows) comes from the pre-tiled gate
-//      matrix [E16/16][H/32][64 lanes][8] (one contiguous 1 KiB per wave load),
-//      in batches of NG_U steps, the next batch in flight while one computes;
-//      the B operand is built from LDS: y = x * gamma, exact in fp32 (two
-//      8-bit mantissas), split into hi = bf16(y) and lo = bf16(y - hi), two
-//      MFMAs per step, so the dot products see y to ~16 bits.
-//   3. Partial sums of a tile meet in LDS and are added in fixed order, then
-//      scaled by the row's fp32 inverse RMS: logit = rinv * (W_g . y), the
-//      gate of the fp32 normed row.
+//   2. Wave w takes the k-steps j = w, w + 8, ... of every expert tile of the
+//      block. The B operand is built once per step from LDS: y = x * gamma,
+//      exact in fp32 (two 8-bit mantissas), split into hi = bf16(y) and
+//      lo = bf16(y - hi), so the dot products see y to ~16 bits; each expert
+//      tile then takes two MFMAs with its A operand (gate rows from the
+//      pre-tiled gate matrix [E16/16][H/32][64 lanes][8], one contiguous 1 KiB
+//      per wave load), loaded in batches of NG_F fragments, the next batch in
+//      flight while one computes.
+//   3. The 8 partial sums of a tile meet in LDS (over the staged rows, which
+//      are dead by then) and are added in wave order, then scaled by the row's
+//      fp32 inverse RMS: logit = rinv * (W_g . y), the gate of the fp32 normed
+//      row.
 //   The residual copy and normed = bf16(n) are written by all blocks of a
 //   token group, each taking one contiguous range of 16-byte column chunks.
 // ---------------------------------------------------------------------------
-// LDS of one block: 16 rows of H + 8, gamma, partial sums, 16 inverse RMS.
 constexpr size_t NG_LDS_MAX = 160 * 1024;
-constexpr int NG_U = 8;   // gate k-steps per load batch
+constexpr int NG_F = 16;  // gate fragments per load batch
 constexpr int NG_NB = 8;  // 16-byte chunks per lane and row in one load round
+
+// LDS of one block: 16 rows of H + 8 (later the 8 x ET partial-sum tiles),
+// gamma, 16 inverse RMS.
+inline size_t norm_gate_lds_bytes(int H, int et) {
+  const size_t rows = (size_t)16 * (H + 8) * 2, red = (size_t)8 * et * 64 * 16;
+  return std::max(rows, red) + (size_t)H * 2 + 16 * 4;
+}
 
 template <int ET>
 __global__ void __launch_bounds__(512) norm_gate_lds_kernel(const bf16* __restrict__ hidden,
@@ -611,32 +619,34 @@ __global__ void __launch_bounds__(512) norm_gate_lds_kernel(const bf16* __restri
                                                             float* __restrict__ logits, int n,
                                                             int H, int E, float eps) {
   extern __shared__ __attribute__((aligned(16))) unsigned char ng_smem[];
-  constexpr int KS = 8 / ET;  // waves per expert tile (k-split)
+  constexpr int U = NG_F / ET;  // k-steps per batch
   const int HP = H + 8;
-  bf16* xs = (bf16*)ng_smem;                        // [16][HP]
-  bf16* gs = xs + 16 * HP;                          // [H]
-  floatx4* red = (floatx4*)(gs + H);                // [8][64]
-  float* rinv = (float*)(red + 8 * 64);             // [16]
+  const size_t rows_bytes = std::max((size_t)16 * HP * 2, (size_t)8 * ET * 64 * 16);
+  bf16* xs = (bf16*)ng_smem;                          // [16][HP]
+  floatx4* red = (floatx4*)ng_smem;                   // [8][ET][64], after the rows
+  bf16* gs = (bf16*)(ng_smem + rows_bytes);           // [H]
+  float* rinv = (float*)(gs + H);                     // [16]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * 16;
   // this block's share of the 16-byte column chunks for the residual and normed copies
   const int nch = H >> 3;
   const int c_lo = blockIdx.y * nch / gridDim.y, c_hi = (blockIdx.y + 1) * nch / gridDim.y;
 
-  // 0. first batch of gate fragments: expert tile et, k-steps ks, ks + KS, ...
-  const int et = wave % ET, ks = wave / ET;
-  const int tile = blockIdx.y * ET + et;
+  // 0. first batch of gate fragments: k-steps wave, wave + 8, ... of tiles
+  // blockIdx.y * ET + 0 .. ET-1
   const int nsteps = H / 32;
-  const bf16* wt = wgate_t + ((size_t)tile * nsteps * 64 + lane) * 8;
-  auto load_batch = [&](bf16x8 (&wf)[NG_U], int j0) {
+  const bf16* wt = wgate_t + ((size_t)blockIdx.y * ET * nsteps * 64 + lane) * 8;
+  auto load_batch = [&](bf16x8 (&wf)[U][ET], int j0) {
 #pragma unroll
-    for (int u = 0; u < NG_U; ++u) {
-      const int j = min(j0 + u * KS, nsteps - 1);  // past the end: a valid step, not used
-      wf[u] = *(const bf16x8*)(wt + (size_t)j * 512);
+    for (int u = 0; u < U; ++u) {
+      const int j = min(j0 + u * 8, nsteps - 1);  // past the end: a valid step, not used
+#pragma unroll
+      for (int et = 0; et < ET; ++et)
+        wf[u][et] = *(const bf16x8*)(wt + ((size_t)et * nsteps + j) * 512);
     }
   };
-  bf16x8 wa[NG_U], wb[NG_U];
-  load_batch(wa, ks);
+  bf16x8 wa[U][ET], wb[U][ET];
+  load_batch(wa, wave);
 
   // 1. gamma and rows -> LDS (wave w: rows 2w, 2w+1), residual copy, sums of squares
   for (int i = tid * 8; i < H; i += 512 * 8) *(bf16x8*)(gs + i) = *(const bf16x8*)(gamma + i);
@@ -682,16 +692,18 @@ __global__ void __launch_bounds__(512) norm_gate_lds_kernel(const bf16* __restri
   }
   __syncthreads();
 
-  // 2. gate: batches of NG_U k-steps, the next batch loading while one computes
+  // 2. gate: every expert tile of the block from one split of each k-step
   const int tok = lane & 15, kg = lane >> 4;
   const float rv = rinv[tok];
   const bf16* xrow = xs + tok * HP + kg * 8;
   const bf16* grow = gs + kg * 8;
-  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-  auto compute_batch = [&](const bf16x8 (&wf)[NG_U], int j0) {
+  floatx4 acc[ET];
 #pragma unroll
-    for (int u = 0; u < NG_U; ++u) {
-      const int j = j0 + u * KS;
+  for (int et = 0; et < ET; ++et) acc[et] = floatx4{0.f, 0.f, 0.f, 0.f};
+  auto compute_batch = [&](const bf16x8 (&wf)[U][ET], int j0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * 8;
       if (j >= nsteps) break;
       const bf16x8 xv = *(const bf16x8*)(xrow + j * 32);
       const bf16x8 gv = *(const bf16x8*)(grow + j * 32);
@@ -702,19 +714,21 @@ __global__ void __launch_bounds__(512) norm_gate_lds_kernel(const bf16* __restri
         hi[q] = (bf16)v;
         lo[q] = (bf16)(v - (float)hi[q]);
       }
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u], hi, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u], lo, acc, 0, 0, 0);
+#pragma unroll
+      for (int et = 0; et < ET; ++et) {
+        acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u][et], hi, acc[et], 0, 0, 0);
+        acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u][et], lo, acc[et], 0, 0, 0);
+      }
     }
   };
-  constexpr int BS = KS * NG_U;  // k-steps between consecutive batches of a wave
-  for (int j0 = ks; j0 < nsteps; j0 += 2 * BS) {
+  constexpr int BS = 8 * U;  // k-steps between consecutive batches of a wave
+  for (int j0 = wave; j0 < nsteps; j0 += 2 * BS) {
     if (j0 + BS < nsteps) load_batch(wb, j0 + BS);
     compute_batch(wa, j0);
     if (j0 + BS >= nsteps) break;
     if (j0 + 2 * BS < nsteps) load_batch(wa, j0 + 2 * BS);
     compute_batch(wb, j0 + BS);
   }
-  red[wave * 64 + lane] = acc;
 
   // normed rows: wave w rows 2w, 2w+1, this block's column chunks, from LDS
 #pragma unroll
@@ -732,13 +746,16 @@ __global__ void __launch_bounds__(512) norm_gate_lds_kernel(const bf16* __restri
       *(bf16x8*)(normed + (size_t)(t0 + r) * H + i) = o;
     }
   }
+  __syncthreads();  // every wave is done with the staged rows
+#pragma unroll
+  for (int et = 0; et < ET; ++et) red[(wave * ET + et) * 64 + lane] = acc[et];
   __syncthreads();
 
-  // 3. tile et's KS partial sums in order (waves et, et + ET, ...)
+  // 3. tile et: the 8 waves' partial sums in wave order
   if (wave < ET) {
     floatx4 v = red[wave * 64 + lane];
 #pragma unroll
-    for (int k2 = 1; k2 < KS; ++k2) v += red[(wave + k2 * ET) * 64 + lane];
+    for (int w = 1; w < 8; ++w) v += red[(w * ET + wave) * 64 + lane];
     v *= rv;  // the row's inverse RMS, in fp32
     const int e = (blockIdx.y * ET + wave) * 16 + 4 * kg;
     if (t0 + tok < n && e < E) {
@@ -888,13 +905,13 @@ static void norm_gate_tm(int act_dt, const void* hidden, const void* gamma, cons
 hipError_t launch_norm_gate(int act_dt, const void* hidden, const void* gamma, const void* wgate,
                             const void* wgate_t, void* normed, void* residual, float* logits,
                             int n, int H, int E, float eps, hipStream_t s) {
-  const size_t lds = (size_t)16 * (H + 8) * 2 + (size_t)H * 2 + 8 * 64 * 16 + 16 * 4;
+  // Expert tiles per block: fewer as the token groups shrink, so that the
+  // grid keeps >= 256 blocks where the tiles allow.
+  const int bx = (n + 15) / 16, tiles = (E + 15) / 16;
+  int et = 8;
+  while (et > 1 && (tiles % et != 0 || bx * (tiles / et) < 256)) et /= 2;
+  const size_t lds = norm_gate_lds_bytes(H, et);
   if (act_dt == MOE_DT_BF16 && wgate_t && lds <= NG_LDS_MAX) {
-    // Expert tiles per block: fewer as the token groups shrink, so that the
-    // grid keeps >= 256 blocks where the tiles allow.
-    const int bx = (n + 15) / 16, tiles = (E + 15) / 16;
-    int et = 8;
-    while (et > 1 && (tiles % et != 0 || bx * (tiles / et) < 256)) et /= 2;
     static bool attr_set = false;  // the dynamic LDS exceeds the 64 KiB default
     if (!attr_set) {
       hipError_t e = hipSuccess;

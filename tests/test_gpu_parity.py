@@ -376,6 +376,20 @@ def test_small_nvfp4_decode_sizes(ml, n):
     pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"])
 
 
+def test_wide_tiles_nvfp4_sampled(ml):
+    # NVFP4 weights on 128-row tiles with 8 waves per workgroup and the
+    # 3-stage ring (grouped up: 512 rows per expert, 16 feature tiles of 256)
+    # next to 4-wave ones (grouped down, shared). All ids, sampled output rows.
+    wl = wlm.Workload("wide_tiles_nvfp4", H=512, E=8, k=2, I=4096, S=512, L=0, N=2048,
+                      expert_dtype="nvfp4")
+    r = run_layer(ml, wl, wl.N, seed=9)
+    Wn = pu.oracle_weights(r["W"], nvfp4=True)
+    ref_ids, margin, _ = pu.oracle_routing(r["x"], Wn, wl)
+    pu.check_ids(r["ids"], ref_ids, margin)
+    rows = _sample_rows(wl.N, 48, 3)
+    print("errors", pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"], rows=rows))
+
+
 @pytest.mark.slow
 def test_full_size_nvfp4_sampled(ml):
     wl = wlm.WORKLOADS["nvfp4_direct"]
