@@ -271,15 +271,15 @@ template <int FT, bool NT> struct WSrc<1, FT, NT> {
 // Pipeline depth S: the loads of step k+S-1 are issued at the start of step
 // k, and a gathered activation slice waits one more step in registers before
 // it goes to LDS.
-// Measured on the layer's shapes: three stages pay on 128 x 256 tiles (7-9%
-// on the bf16 grouped GEMMs from 4096 tokens up, 2% on the latent layer, 1%
-// on NVFP4 weights at 4096 tokens) and on
-// DEEP launches (dense, at most one 128 x 128 tile per CU, so one resident
-// workgroup per CU and the register budget of a whole SIMD: 8-10% on the
-// shared expert at 1024 tokens); two elsewhere (three cost 2-5% on 64-row
-// tiles, and spill at two 128 x 128 workgroups per CU).
+// Measured on the layer's shapes: three stages pay on 128 x 256 and 128 x 192
+// tiles (7-9% on the bf16 grouped GEMMs from 4096 tokens up, 2% on the latent
+// layer, 1% on NVFP4 weights at 4096 tokens) and on DEEP launches (dense, at
+// most one 128 x 128 tile per CU, so one resident workgroup per CU and the
+// register budget of a whole SIMD: 8-10% on the shared expert at 1024
+// tokens); two elsewhere (three cost 2-5% on 64-row tiles, and spill at two
+// 128 x 128 workgroups per CU).
 constexpr int mfma_stages(int bmt, int nw, bool deep) {
-  return deep || (bmt == 128 && nw == 8) ? 3 : 2;
+  return deep || (bmt == 128 && nw >= 6) ? 3 : 2;
 }
 // Workgroups per CU the register budget is sized for.
 constexpr int mfma_min_blocks(int bmt, int nw, bool deep) {
@@ -590,6 +590,14 @@ static hipError_t launch_mfma_wq(const GemmArgs& a, MfmaCfg cfg, int epi, int sl
     // up projections at 4096 tokens, 8-16% slower for 2688-wide down ones).
     const bool dense8 = !G && items8 >= (long long)cus &&
                         (a.N % 256 == 0 || 2 * items8 >= 3LL * cus);
+    // Weight-streaming grouped bf16 launches (each expert one row tile) whose
+    // width is a multiple of 192 but not of 256 take 6 waves (192 features per
+    // workgroup): no half-dead last feature tile, and whole rounds of items per
+    // XCD (2688-wide down projection at 1024 tokens: 238 -> 229 us). Where the
+    // MFMAs bound the launch, the uneven waves per SIMD cost 10-20%.
+    if constexpr (G && NT && WQ == 0)
+      if (a.N % 192 == 0 && a.N % 256 != 0 && items8 >= 2LL * cus)
+        return launch_mfma_shape<32, 128, 6, WQ, G, NT>(a, epi, slots, s);
     if (items8 >= 2LL * cus || dense8)
       return launch_mfma_shape<32, 128, 8, WQ, G, NT>(a, epi, slots, s);
     // A dense bf16 launch with at most one tile per CU runs one workgroup per

@@ -350,6 +350,16 @@ def test_wide_tiles_sampled(ml):
     print("errors", pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"], rows=rows))
 
 
+def test_six_wave_tiles(ml):
+    # Grouped down projection 1344 = 7 x 192 wide with one 128-row tile per
+    # expert (64 rows each): 6-wave workgroups, 4 k-steps (the 3-stage ring's
+    # tail only). Every token compared.
+    wl = wlm.Workload("six_wave", H=1344, E=64, k=4, I=256, S=128, L=0, N=1024)
+    r = run_layer(ml, wl, wl.N, seed=10)
+    Wn = pu.oracle_weights(r["W"])
+    print("errors", pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"]))
+
+
 NVFP4_SMALL = {
     "nvfp4_direct": wlm.Workload("nvfp4_direct_s", H=512, E=16, k=4, I=192, S=320, L=0, N=150,
                                  expert_dtype="nvfp4"),
