@@ -236,15 +236,17 @@ int upload_nvfp4(moe_layer* L, void** q, void** sc, float** s2, const moe_nvfp4_
 
 // Grouped launches: the row-tile height follows the mean rows per expert, so
 // that most experts take one tile and few rows are padding. From 41 rows per
-// expert on, 128-row tiles: at 48 (1024 tokens, 128 experts, top-6) a fifth of
-// the experts exceed 64 rows, and a second 64-row tile streams that expert's
-// weights again and unbalances the XCDs' tile ranges; one 128-row tile per
-// expert measured 7% faster on the up GEMM (the padding rows cost only MFMA
-// time, which the weight stream leaves idle).
-MfmaCfg grouped_cfg(int rows_per_group) {
+// expert on, 128-row tiles where there are 64 experts or more: at 48 (1024
+// tokens, 128 experts, top-6) a fifth of the experts exceed 64 rows, and a
+// second 64-row tile streams that expert's weights again and unbalances the
+// XCDs' tile ranges; one 128-row tile per expert measured 7% faster on the up
+// GEMM (the padding rows cost only MFMA time, which the weight stream leaves
+// idle). With fewer experts (one GPU's expert shard: 16) the 128-row grid is
+// too small to fill the chip and 64-row tiles stay 3% faster.
+MfmaCfg grouped_cfg(int rows_per_group, int experts) {
   if (rows_per_group <= 16) return {16, 16};
   if (rows_per_group <= 32) return {32, 32};
-  if (rows_per_group <= 40) return {32, 64};
+  if (rows_per_group <= 40 || (rows_per_group <= 80 && experts < 64)) return {32, 64};
   return {32, 128};
 }
 
@@ -569,7 +571,7 @@ int moe_layer_forward(moe_layer_t* L, void* hidden, void* residual, int32_t n, v
     StageScope sc(L, MOE_STAGE_TOPK, s);
     HIP_TRY(launch_topk(L->logits, n, E, k, c.routed_scaling_factor, L->ids, L->w, s));
   }
-  const MfmaCfg gc = grouped_cfg((R + E - 1) / E);
+  const MfmaCfg gc = grouped_cfg((R + E - 1) / E, E);
   const int bm = bf ? gc.bmt : 64;
   {
     StageScope sc(L, MOE_STAGE_SORT, s);
