@@ -590,14 +590,24 @@ static hipError_t launch_mfma_wq(const GemmArgs& a, MfmaCfg cfg, int epi, int sl
     // up projections at 4096 tokens, 8-16% slower for 2688-wide down ones).
     const bool dense8 = !G && items8 >= (long long)cus &&
                         (a.N % 256 == 0 || 2 * items8 >= 3LL * cus);
-    // Weight-streaming grouped bf16 launches (each expert one row tile) whose
-    // width is a multiple of 192 but not of 256 take 6 waves (192 features per
-    // workgroup): no half-dead last feature tile, and whole rounds of items per
-    // XCD (2688-wide down projection at 1024 tokens: 238 -> 229 us). Where the
-    // MFMAs bound the launch, the uneven waves per SIMD cost 10-20%.
+    // Weight-streaming grouped bf16 launches (each expert one row tile) take
+    // 6 waves (192 features per workgroup) where that needs less time per XCD
+    // than 8, with one workgroup per CU either way: rounds of items x (features
+    // per item + a fixed 128-feature equivalent per item), a fit to the two
+    // projections at 1024 and 2048 tokens. The 2688-wide down projection goes
+    // from 6 rounds of 256 (last feature tile half dead) to 7 of 192 (238 ->
+    // 224 us); the 1856-wide up projection keeps 4 rounds of 256 (5 of 192
+    // measured 218 -> 225 us). Where the MFMAs bound the launch, the uneven
+    // waves per SIMD cost 10-20%, so NVFP4 weights and multi-tile experts keep
+    // 8 waves.
     if constexpr (G && NT && WQ == 0)
-      if (a.N % 192 == 0 && a.N % 256 != 0 && items8 >= 2LL * cus)
-        return launch_mfma_shape<32, 128, 6, WQ, G, NT>(a, epi, slots, s);
+      if (cfg.est_tiles > 0 && items8 >= 2LL * cus) {
+        const long long t = (cfg.est_tiles + 7) / 8, w = std::max(1, cus / 8);
+        auto cost = [&](long long width) {
+          return (t * ((a.N + width - 1) / width) + w - 1) / w * (width + 128);
+        };
+        if (cost(192) < cost(256)) return launch_mfma_shape<32, 128, 6, WQ, G, NT>(a, epi, slots, s);
+      }
     if (items8 >= 2LL * cus || dense8)
       return launch_mfma_shape<32, 128, 8, WQ, G, NT>(a, epi, slots, s);
     // A dense bf16 launch with at most one tile per CU runs one workgroup per

@@ -72,6 +72,7 @@ hipError_t launch_gemm_simt_f32(const GemmArgs& a, int epi, int grid_y, hipStrea
 struct MfmaCfg {
   int wf;   // features per wave (16, 32)
   int bmt;  // rows (tokens / routes) per workgroup tile (16, 32, 64, 128)
+  int est_tiles = 0;  // grouped launches: expected live row tiles (0 = unknown)
 };
 // `slots` = row tiles (grouped: tile-list capacity, live count read on device).
 // stream_weights (grouped launches only): non-temporal weight loads, for

@@ -571,7 +571,7 @@ int moe_layer_forward(moe_layer_t* L, void* hidden, void* residual, int32_t n, v
     StageScope sc(L, MOE_STAGE_TOPK, s);
     HIP_TRY(launch_topk(L->logits, n, E, k, c.routed_scaling_factor, L->ids, L->w, s));
   }
-  const MfmaCfg gc = grouped_cfg((R + E - 1) / E, E);
+  MfmaCfg gc = grouped_cfg((R + E - 1) / E, E);
   const int bm = bf ? gc.bmt : 64;
   {
     StageScope sc(L, MOE_STAGE_SORT, s);
@@ -581,6 +581,7 @@ int moe_layer_forward(moe_layer_t* L, void* hidden, void* residual, int32_t n, v
   const int tiles_cap = (R + bm - 1) / bm + std::min(E, R);
   // Experts expected to fit one row tile: each weight byte is read once.
   const bool one_tile = (long long)((R + E - 1) / E) * 4 <= (long long)bm * 3;
+  if (one_tile) gc.est_tiles = std::min(E, R);
 
   if (side) HIP_TRY(hipStreamWaitEvent(s, L->ev_join, 0));
 
