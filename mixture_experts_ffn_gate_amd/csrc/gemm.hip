@@ -643,9 +643,10 @@ hipError_t launch_gemm_mfma(const GemmArgs& a, MfmaCfg cfg, int epi, bool tc_bf1
 // One launch covers up to two segments: the routed experts (grouped, tile
 // list) and the shared expert (dense), so small batches need no side stream.
 // Item = (segment, row tile, 16-feature tile); one workgroup per item; the 4
-// waves split the k-steps of the item and each issues the loads of GU steps
-// at a time (weights and the <= 16 activation rows straight from memory into
-// MFMA registers), so many loads are in flight per CU even for one token.
+// waves take the item's k-steps in interleaved groups of GU and each issues
+// the loads of a whole group at a time (weights and the <= 16 activation rows
+// straight from memory into MFMA registers), so many loads are in flight per
+// CU even for one token.
 // The partial sums meet in LDS and are added in wave order (deterministic).
 // ---------------------------------------------------------------------------
 struct GemvArgs {
@@ -678,7 +679,6 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemvArgs g) {
   if (!decode_tile(a, slot, 16, ti)) return;  // uniform: the whole workgroup leaves
 
   const int nsteps = a.K / 64;
-  const int s0 = wave * nsteps / 4, s1 = (wave + 1) * nsteps / 4;
   const int nf0 = ftile * 16;
   Src src;
   src.init(a, ti.g, nf0, lane);
@@ -686,12 +686,15 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemvArgs g) {
   const bf16* xp = (const bf16*)a.A + (size_t)a_row_of(a, ti.row0 + r) * a.lda + (lane >> 4) * 8;
 
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int kb = s0; kb < s1; kb += GU) {
+  // Load groups of GU k-steps dealt round-robin to the 4 waves: at any time
+  // the workgroup reads one contiguous run of its 16-feature tile (measured
+  // 1% faster at 1-16 tokens than 4 separate quarter-K streams).
+  for (int kb = wave * GU; kb < nsteps; kb += 4 * GU) {
     Frag w[GU];
     bf16x8 x[GU][2];
 #pragma unroll
     for (int u = 0; u < GU; ++u) {
-      const int ks = min(kb + u, s1 - 1);  // past the range: a valid step, not used
+      const int ks = min(kb + u, nsteps - 1);  // past the end: a valid step, not used
       src.load(w[u], ks);
       x[u][0] = *(const bf16x8*)(xp + ks * 64);
       x[u][1] = *(const bf16x8*)(xp + ks * 64 + 32);
@@ -699,7 +702,7 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemvArgs g) {
     __builtin_amdgcn_sched_barrier(0);  // all GU steps' loads issue before any MFMA
 #pragma unroll
     for (int u = 0; u < GU; ++u) {
-      if (kb + u >= s1) break;
+      if (kb + u >= nsteps) break;
 #pragma unroll
       for (int s = 0; s < 2; ++s)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(src.get(w[u], 0, s, lane), x[u][s], acc, 0,
