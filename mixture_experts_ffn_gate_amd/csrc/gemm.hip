@@ -199,7 +199,9 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t q, float sc) {
 // Weight fragment sources of the MFMA kernel. A fragment is what one wave
 // consumes per 64-wide k-step for its FT 16-row tiles.
 //  * bf16: pre-tiled [N/16][K/32][64 lanes][8]: lane l holds row l%16, k
-//    8*(l/16)..+7 of a 16x32 block (1 KiB per block, one contiguous read).
+//    8*(l/16)..+7 of a 16x32 block (1 KiB per block, one contiguous read);
+//    or k-major [K/64][N/16][2][64][8] (b_kmajor: a workgroup's tiles of one
+//    k-step form one contiguous run).
 //  * NVFP4: pre-tiled packed nibbles [N/16][K/64][64 lanes][8 bytes] (dword s
 //    holds the lane's 8 codes of k-chunk s) and block scales
 //    [N/16][K/64][16 rows][4 bytes] (the row's four 16-element blocks of the
@@ -213,6 +215,7 @@ template <int FT, bool NT> struct WSrc<0, FT, NT> {
   struct Frag { bf16x8 v[FT][2]; };
   const bf16* p[FT];
   int step[FT];  // elements per 64-wide k-step (0 for a dead tile)
+  int soff[FT];  // elements between the two 32-wide halves of a step (0 for a dead tile)
   __device__ __forceinline__ void init(const GemmArgs& a, int g, int nf0, int lane) {
     const bf16* W = (const bf16*)a.B + (size_t)g * a.b_gstride;
     const int KC = a.K / 32;
@@ -220,8 +223,14 @@ template <int FT, bool NT> struct WSrc<0, FT, NT> {
     for (int ft = 0; ft < FT; ++ft) {
       const int rt = (nf0 >> 4) + ft;
       const bool live = rt * 16 < a.N;
-      p[ft] = live ? W + ((size_t)rt * KC * 64 + lane) * 8 : W;
-      step[ft] = live ? 1024 : 0;
+      if (a.b_kmajor) {  // [K/64][N/16][2][64][8]
+        p[ft] = live ? W + ((size_t)rt * 2 * 64 + lane) * 8 : W;
+        step[ft] = live ? (a.N / 16) * 1024 : 0;
+      } else {  // [N/16][K/32][64][8]
+        p[ft] = live ? W + ((size_t)rt * KC * 64 + lane) * 8 : W;
+        step[ft] = live ? 1024 : 0;
+      }
+      soff[ft] = live ? 512 : 0;
     }
   }
   __device__ __forceinline__ void load(Frag& f, int ks) const {
@@ -229,7 +238,7 @@ template <int FT, bool NT> struct WSrc<0, FT, NT> {
     for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-        f.v[ft][s] = ld_w<NT>((const bf16x8*)(p[ft] + (size_t)ks * step[ft] + s * (step[ft] >> 1)));
+        f.v[ft][s] = ld_w<NT>((const bf16x8*)(p[ft] + (size_t)ks * step[ft] + s * soff[ft]));
   }
   __device__ __forceinline__ bf16x8 get(const Frag& f, int ft, int s, int) const { return f.v[ft][s]; }
 };
@@ -766,31 +775,45 @@ hipError_t launch_gemv(const GemmArgs* segs, const int* slots, int nseg, int epi
 }
 
 // ---------------------------------------------------------------------------
-// Re-tile [G][N][K] row-major bf16 into [G][N/16][K/32][64][8] (MFMA A-operand
-// lane order). One thread per 16-byte destination chunk.
+// Re-tile [G][N][K] row-major bf16 into the MFMA A-operand lane order:
+// feature-major [G][N/16][K/32][64][8] or k-major [G][K/64][N/16][2][64][8].
+// One thread per 16-byte destination chunk.
 // ---------------------------------------------------------------------------
 __global__ void retile_bf16_kernel(const bf16* __restrict__ src, bf16* __restrict__ dst, int G,
-                                   int N, int K) {
+                                   int N, int K, int kmajor) {
   const size_t chunks = (size_t)G * N * K / 8;
-  const int KC = K / 32, NT = N / 16;
+  const int KC = K / 32, NT = N / 16, KS = K / 64;
   for (size_t c = blockIdx.x * (size_t)blockDim.x + threadIdx.x; c < chunks;
        c += (size_t)gridDim.x * blockDim.x) {
     const int lane = (int)(c & 63);
-    size_t blk = c >> 6;  // (g, rt, kc)
-    const int kc = (int)(blk % KC);
-    blk /= KC;
-    const int rt = (int)(blk % NT);
-    const size_t g = blk / NT;
+    size_t blk = c >> 6;
+    int kc, rt;
+    size_t g;
+    if (kmajor) {  // (g, ks, rt, s)
+      const int s = (int)(blk & 1);
+      blk >>= 1;
+      rt = (int)(blk % NT);
+      blk /= NT;
+      kc = (int)(blk % KS) * 2 + s;
+      g = blk / KS;
+    } else {  // (g, rt, kc)
+      kc = (int)(blk % KC);
+      blk /= KC;
+      rt = (int)(blk % NT);
+      g = blk / NT;
+    }
     const int row = rt * 16 + (lane & 15);
     const int k = kc * 32 + 8 * (lane >> 4);
     *(bf16x8*)(dst + c * 8) = *(const bf16x8*)(src + (g * N + row) * (size_t)K + k);
   }
 }
 
-hipError_t launch_retile_bf16(const bf16* src, bf16* dst, int G, int N, int K, hipStream_t s) {
+hipError_t launch_retile_bf16(const bf16* src, bf16* dst, int G, int N, int K, bool kmajor,
+                              hipStream_t s) {
   const size_t chunks = (size_t)G * N * K / 8;
   const int blocks = (int)std::min<size_t>((chunks + 255) / 256, 65536);
-  hipLaunchKernelGGL(retile_bf16_kernel, dim3(blocks), dim3(256), 0, s, src, dst, G, N, K);
+  hipLaunchKernelGGL(retile_bf16_kernel, dim3(blocks), dim3(256), 0, s, src, dst, G, N, K,
+                     kmajor ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -39,6 +39,7 @@ struct GemmArgs {
   int bm;
   const void* res;
   const void* add;  // EPI_ADD_RES second addend, C's dtype (may be null)
+  int b_kmajor;     // bf16 weights in the k-major tile order (see launch_retile_bf16)
 };
 
 // RMSNorm + residual + gate logits. wgate_t (bf16 layers, may be null) is the
@@ -87,7 +88,12 @@ hipError_t launch_gemv(const GemmArgs* segs, const int* slots, int nseg, int epi
                        hipStream_t s);
 
 // Re-tile bf16 [G][N][K] row-major weights into the MFMA lane order.
-hipError_t launch_retile_bf16(const bf16* src, bf16* dst, int G, int N, int K, hipStream_t s);
+// Re-tile bf16 [G][N][K] into the MFMA lane order of 16-feature x 32-k blocks
+// (lane l: row l%16, k 8*(l/16)..+7). Feature-major: [G][N/16][K/32][64][8],
+// each 16-feature tile contiguous along K. k-major: [G][K/64][N/16][2][64][8],
+// all tiles of one 64-wide k-step contiguous.
+hipError_t launch_retile_bf16(const bf16* src, bf16* dst, int G, int N, int K, bool kmajor,
+                              hipStream_t s);
 
 // Re-tile NVFP4 [G][N][K/2] packed + [G][N][K/16] scales into the MFMA lane order.
 hipError_t launch_retile_nvfp4(const uint8_t* qsrc, const uint8_t* ssrc, uint8_t* qdst,

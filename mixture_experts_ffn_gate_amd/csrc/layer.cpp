@@ -204,14 +204,14 @@ int check_config(const moe_layer_config_t& c) {
 // Copy a weight matrix stack [G][N][K] into layer memory: bf16 is re-tiled for
 // the MFMA kernels, fp32 is copied as is.
 int upload_proj(moe_layer* L, void** dst, const void* src, int G, int N, int K, bool retile,
-                hipStream_t s, const char* name) {
+                hipStream_t s, const char* name, bool kmajor = false) {
   if (!src) return fail(MOE_ERR_INVALID_ARG, "weight '%s' is NULL", name);
   const size_t elems = (size_t)G * N * K;
   const size_t bytes = elems * (L->mfma ? 2 : 4);
   int rc = dalloc(L, dst, bytes);
   if (rc) return rc;
   if (retile) {
-    HIP_TRY(launch_retile_bf16((const bf16*)src, (bf16*)*dst, G, N, K, s));
+    HIP_TRY(launch_retile_bf16((const bf16*)src, (bf16*)*dst, G, N, K, kmajor, s));
   } else {
     HIP_TRY(hipMemcpyAsync(*dst, src, bytes, hipMemcpyDeviceToDevice, s));
   }
@@ -280,6 +280,10 @@ void set_weights(const moe_layer* L, GemmArgs& a, const void* w, const void* sc,
     a.b_scale2 = s2;
   } else {
     a.b_gstride = (long long)N * K;
+    // The down projections are stored k-major (all 16-feature tiles of a k-step
+    // contiguous): measured 2% faster on the down GEMMs, but 6% slower on the
+    // latent up GEMM and 1% on the decode up GEMV, which keep feature-major.
+    a.b_kmajor = L->mfma && (w == L->down || w == L->sh_down);
   }
 }
 
@@ -428,7 +432,7 @@ int moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_weights_t* w
     TRYH(hipMemsetAsync(padded, 0, e16 * H * 2, s));
     TRYH(hipMemcpyAsync(padded, wts->gate, (size_t)E * H * 2, hipMemcpyDeviceToDevice, s));
     TRY(dalloc(L, &L->gate_t, e16 * H * 2));
-    TRYH(launch_retile_bf16((const bf16*)padded, (bf16*)L->gate_t, 1, (int)e16, H, s));
+    TRYH(launch_retile_bf16((const bf16*)padded, (bf16*)L->gate_t, 1, (int)e16, H, false, s));
     TRYH(hipStreamSynchronize(s));
     TRY(dfree(L, padded));
   }
@@ -447,10 +451,10 @@ int moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_weights_t* w
     }
   } else {
     TRY(upload_proj(L, &L->up, wts->up, E, I, D, L->mfma, s, "up"));
-    TRY(upload_proj(L, &L->down, wts->down, E, D, I, L->mfma, s, "down"));
+    TRY(upload_proj(L, &L->down, wts->down, E, D, I, L->mfma, s, "down", true));
     if (S > 0) {
       TRY(upload_proj(L, &L->sh_up, wts->shared_up, 1, S, H, L->mfma, s, "shared_up"));
-      TRY(upload_proj(L, &L->sh_down, wts->shared_down, 1, H, S, L->mfma, s, "shared_down"));
+      TRY(upload_proj(L, &L->sh_down, wts->shared_down, 1, H, S, L->mfma, s, "shared_down", true));
     }
   }
   // Workspace.
