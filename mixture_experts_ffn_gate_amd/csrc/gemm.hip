@@ -34,6 +34,7 @@
 // Decode-sized GEMV (gemv_kernel): one workgroup per (row tile of <= 16 rows,
 // 16 features); see below.
 #include <algorithm>
+#include <type_traits>
 #include <utility>
 
 #include "kernels.h"
@@ -209,13 +210,14 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t q, float sc) {
 template <int WQ, int FT, bool NT> struct WSrc;
 
 // Dead tiles (features past N, possible in the last feature tile) keep the
-// loads unconditional but point every lane at one fixed 16-byte chunk with a
-// zero step: one cached line instead of a re-read of live weights.
+// loads unconditional but point every lane at two fixed 1 KiB blocks at the
+// start of the group with a zero step: cached lines instead of a re-read of
+// live weights. The two 32-wide halves of a step are 512 elements apart in
+// both tile orders.
 template <int FT, bool NT> struct WSrc<0, FT, NT> {
   struct Frag { bf16x8 v[FT][2]; };
   const bf16* p[FT];
   int step[FT];  // elements per 64-wide k-step (0 for a dead tile)
-  int soff[FT];  // elements between the two 32-wide halves of a step (0 for a dead tile)
   __device__ __forceinline__ void init(const GemmArgs& a, int g, int nf0, int lane) {
     const bf16* W = (const bf16*)a.B + (size_t)g * a.b_gstride;
     const int KC = a.K / 32;
@@ -230,7 +232,6 @@ template <int FT, bool NT> struct WSrc<0, FT, NT> {
         p[ft] = live ? W + ((size_t)rt * KC * 64 + lane) * 8 : W;
         step[ft] = live ? 1024 : 0;
       }
-      soff[ft] = live ? 512 : 0;
     }
   }
   __device__ __forceinline__ void load(Frag& f, int ks) const {
@@ -238,7 +239,7 @@ template <int FT, bool NT> struct WSrc<0, FT, NT> {
     for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-        f.v[ft][s] = ld_w<NT>((const bf16x8*)(p[ft] + (size_t)ks * step[ft] + s * soff[ft]));
+        f.v[ft][s] = ld_w<NT>((const bf16x8*)(p[ft] + (size_t)ks * step[ft] + s * 512));
   }
   __device__ __forceinline__ bf16x8 get(const Frag& f, int ft, int s, int) const { return f.v[ft][s]; }
 };
@@ -293,6 +294,11 @@ constexpr int mfma_stages(int bmt, int nw, bool deep) {
 // Workgroups per CU the register budget is sized for.
 constexpr int mfma_min_blocks(int bmt, int nw, bool deep) {
   return (bmt >= 128 && nw == 4 && !deep) ? 2 : 1;
+}
+
+// LDS of one workgroup: the activation stages, or the staged output tile.
+constexpr int mfma_lds_elems(int stages, int bmt, int cw) {
+  return stages * bmt * 64 > bmt * (cw + 8) ? stages * bmt * 64 : bmt * (cw + 8);
 }
 
 // One output tile: BMT rows x (NW waves x WF) features.
@@ -427,8 +433,8 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs& a, int slot, int ftile
     // The bf16 tile goes through LDS (row stride CW + 8) and leaves as whole
     // rows: each 16-byte store sits in a contiguous run of CW * 2 bytes per
     // row instead of the accumulator layout's 32-byte pieces (measured 2-6%
-    // faster where the outputs are large). The fp32 residual add of fc2 keeps
-    // the direct path so that it rounds once.
+    // faster where the outputs are large). fc2's residual add stages fp32
+    // instead (below), so that it rounds once.
     constexpr int CW = NW * WF, SP = CW + 8;
     __syncthreads();  // every wave is done with the activation stages
 #pragma unroll
@@ -460,35 +466,57 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs& a, int slot, int ftile
       }
     }
   } else {
+    // fc2: acc + residual + shared, rounded to bf16 once. The fp32 tile goes
+    // through LDS in passes of HR rows (row stride CW + 4 floats) and leaves as
+    // whole rows, so residual, shared and output move as 16-byte row chunks
+    // (the accumulator layout gives each lane 8-byte pieces of 32-byte runs).
+    static_assert(std::is_same<TC, bf16>::value, "the MFMA kernels store bf16");
+    constexpr int CW = NW * WF, SPF = CW + 4;
+    constexpr int CAP = mfma_lds_elems(S, BMT, CW) * 2 / (SPF * 4);  // fp32 rows that fit
+    constexpr int HR = CAP >= BMT ? BMT : CAP >= BMT / 2 ? BMT / 2 : CAP >= BMT / 4 ? BMT / 4 : BMT / 8;
+    static_assert(HR >= 8 && BMT % HR == 0 && HR * SPF * 4 <= mfma_lds_elems(S, BMT, CW) * 2,
+                  "fp32 staging does not fit");
+    float* xf = reinterpret_cast<float*>(xs);
+    const int n0 = ftile * CW;
+    __syncthreads();  // every wave is done with the activation stages
+    for (int h0 = 0; h0 < BMT; h0 += HR) {
 #pragma unroll
-    for (int ft = 0; ft < FT; ++ft) {
-      const int n = nf0 + ft * 16 + 4 * (lane >> 4);
-      if (n >= a.N) continue;
+      for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt) {
-        const int r = tt * 16 + (lane & 15);
-        if (r >= ti.rows) continue;
-        const int p = ti.row0 + r;
-        floatx4 v = acc[ft][tt];
-        if (WQ == 1) v *= s2;
-        if (EPI == EPI_RELU2) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] = relu2(v[q]);
+        for (int tt = 0; tt < TT; ++tt) {
+          const int r = tt * 16 + (lane & 15) - h0;
+          if (r < 0 || r >= HR) continue;
+          floatx4 v = acc[ft][tt];
+          if (WQ == 1) v *= s2;
+          const int c = wave * WF + ft * 16 + 4 * (lane >> 4);
+          *(floatx4*)(&xf[r * SPF + c]) = v;
         }
-        if (EPI == EPI_ADD_RES) {
-          v += store4<TC>::ld((const TC*)a.res + (size_t)p * a.ldc + n);
-          if (a.add) v += store4<TC>::ld((const TC*)a.add + (size_t)p * a.ldc + n);
+      __syncthreads();
+      for (int q = tid; q < HR * (CW / 8); q += NTHR) {
+        const int r = q / (CW / 8), c = (q % (CW / 8)) * 8;
+        if (h0 + r < ti.rows && n0 + c < a.N) {
+          const floatx4 v0 = *(const floatx4*)(&xf[r * SPF + c]);
+          const floatx4 v1 = *(const floatx4*)(&xf[r * SPF + c + 4]);
+          const size_t o = (size_t)(ti.row0 + h0 + r) * a.ldc + n0 + c;
+          const bf16x8 rv = *(const bf16x8*)((const bf16*)a.res + o);
+          float sum[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) sum[i] += (float)rv[i];
+          if (a.add) {
+            const bf16x8 av = *(const bf16x8*)((const bf16*)a.add + o);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sum[i] += (float)av[i];
+          }
+          bf16x8 ob;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) ob[i] = (bf16)sum[i];
+          *(bf16x8*)((bf16*)C + o) = ob;
         }
-        store4<TC>::st(C + (size_t)p * a.ldc + n, v);
       }
+      __syncthreads();
     }
   }
   __syncthreads();  // LDS is reused by the next item
-}
-
-// LDS of one workgroup: the activation stages, or the staged output tile.
-constexpr int mfma_lds_elems(int stages, int bmt, int cw) {
-  return stages * bmt * 64 > bmt * (cw + 8) ? stages * bmt * 64 : bmt * (cw + 8);
 }
 
 template <int WF, int BMT, int NW, int EPI, typename TC, int WQ, bool GROUPED, bool NT,
@@ -568,8 +596,8 @@ static hipError_t launch_mfma_shape(const GemmArgs& a, int epi, int slots, hipSt
     case EPI_STORE:
       return launch_persistent<WF, BMT, NW, EPI_STORE, bf16, WQ, G, NT, DEEP>(a, slots, s);
     case EPI_ADD_RES:  // only the dense fc2 adds residual + shared
-      if (G) return hipErrorInvalidValue;
-      return launch_persistent<WF, BMT, NW, EPI_ADD_RES, bf16, WQ, false, NT, DEEP>(a, slots, s);
+      if constexpr (G) return hipErrorInvalidValue;
+      else return launch_persistent<WF, BMT, NW, EPI_ADD_RES, bf16, WQ, false, NT, DEEP>(a, slots, s);
     default: return hipErrorInvalidValue;
   }
 }
