@@ -75,5 +75,35 @@ def build(verbose: bool = False, extra_flags=(), out: str = LIB, build_dir: str 
     return out
 
 
+def resource_usage(src: str, build_dir: str = BUILD) -> list:
+    """Per-kernel register, scratch and LDS use of one source, from hipcc's
+    kernel-resource-usage remarks: [{"kernel", "vgprs", "agprs", "scratch",
+    "occupancy", "lds"}]. A kernel with scratch > 0 spills registers."""
+    import re
+    import tempfile
+
+    os.makedirs(build_dir, exist_ok=True)
+    with tempfile.TemporaryDirectory(dir=build_dir) as tmp:
+        obj = os.path.join(tmp, "ru.o")
+        cmd = [_hipcc(), *HIP_FLAGS, "--cuda-device-only", "-c", os.path.join(CSRC, src),
+               "-o", obj, "-Rpass-analysis=kernel-resource-usage"]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{res.stderr[-4000:]}")
+    rows = []
+    fields = {"VGPRs": "vgprs", "AGPRs": "agprs", "ScratchSize [bytes/lane]": "scratch",
+              "Occupancy [waves/SIMD]": "occupancy", "LDS Size [bytes/block]": "lds"}
+    for line in res.stderr.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            rows.append({"kernel": m.group(1)})
+            continue
+        for key, name in fields.items():
+            m = re.search(r"remark:\s+" + re.escape(key) + r": (\d+)", line)
+            if m and rows:
+                rows[-1][name] = int(m.group(1))
+    return rows
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
