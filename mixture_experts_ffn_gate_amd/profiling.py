@@ -3,6 +3,7 @@
     python -m mixture_experts_ffn_gate_amd.profiling stats  STATS_CSV  OUT_MD  --cmd "..."
     python -m mixture_experts_ffn_gate_amd.profiling traffic FETCH_CSV WRITE_CSV OUT_JSON \
         --calib-mib 512 --workload NAME --tokens N --cmd "..."
+    python -m mixture_experts_ffn_gate_amd.profiling mfma COUNTER_CSV STATS_CSV OUT_MD --cmd "..."
 
 ``traffic`` reads two ``--pmc`` runs (FETCH_SIZE, then WRITE_SIZE; KiB per
 dispatch) of a ``bench.py --calibrate-copy-mib M`` command. The M MiB
@@ -148,6 +149,45 @@ def traffic(fetch_csv: str, write_csv: str, out_json: str, calib_mib: int, workl
         json.dump(rec, f, indent=1)
 
 
+def mfma(counter_csv: str, stats_csv: str, out_md: str, cmd: str) -> None:
+    """MFMA utilisation of the layer's GEMM kernels from one --pmc run with
+    SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CU_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16
+    and GRBM_GUI_ACTIVE, plus the kernel-trace durations of the same command.
+
+    On gfx950 one MOPS unit is 512 flops and SQ_VALU_MFMA_BUSY_CYCLES counts the
+    issued MFMA work in SIMD-cycles (16 per 16x16x32 bf16 MFMA, 1024 flops per
+    SIMD-cycle), so busy / (4 x SQ_BUSY_CU_CYCLES) is the matrix cores' share
+    of the cycles in which the CUs were busy, and busy / (1024 SIMDs x duration
+    x 2.4 GHz) the share of the chip's nominal MFMA issue rate over the launch.
+    Both count executed MFMAs, padding rows and dead features included."""
+    acc = defaultdict(lambda: defaultdict(list))
+    for r in csv.DictReader(open(counter_csv)):
+        k = short_name(r["Kernel_Name"])
+        if k.startswith(("gemm", "gemv")):
+            acc[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    dur = {short_name(r["Name"]): float(r["AverageNs"]) for r in csv.DictReader(open(stats_csv))}
+    lines = [f"# MFMA utilisation: `{os.path.basename(out_md)}`", "",
+             "Commands (`$REPO` = repository root):", "", "```", cmd, "```", "",
+             "Per launch, averaged over the dispatches of the run (eager forwards under the",
+             "profiler). Executed TFLOP = MOPS x 512; busy/CU = SQ_VALU_MFMA_BUSY_CYCLES /",
+             "(4 x SQ_BUSY_CU_CYCLES); busy/nominal = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x",
+             "duration x 2.4 GHz); both count executed MFMAs (padding rows and dead features",
+             "included).", "",
+             "| kernel | executed GFLOP | MFMA busy (SIMD-cycles) | CU-busy cycles | avg µs | busy/CU | busy/nominal |",
+             "|---|---|---|---|---|---|---|"]
+    for k in sorted(acc, key=lambda x: -dur.get(x, 0.0)):
+        m = {c: sum(v) / len(v) for c, v in acc[k].items()}
+        busy, cu = m.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0), m.get("SQ_BUSY_CU_CYCLES", 0.0)
+        mops = m.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
+        us = dur.get(k, 0.0) / 1e3
+        per_cu = busy / (4 * cu) if cu else float("nan")
+        nominal = busy / (1024 * us * 1e-6 * 2.4e9) if us else float("nan")
+        lines.append(f"| {k} | {mops * 512 / 1e9:.1f} | {busy:.3g} | {cu:.3g} | {us:.1f} | "
+                     f"{per_cu:.2f} | {nominal:.2f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd_name", required=True)
@@ -163,8 +203,15 @@ def main():
     t.add_argument("--workload", required=True)
     t.add_argument("--tokens", type=int, required=True)
     t.add_argument("--cmd", required=True)
+    mf = sub.add_parser("mfma")
+    mf.add_argument("counter_csv")
+    mf.add_argument("stats_csv")
+    mf.add_argument("out")
+    mf.add_argument("--cmd", required=True)
     a = ap.parse_args()
-    if a.cmd_name == "stats":
+    if a.cmd_name == "mfma":
+        mfma(a.counter_csv, a.stats_csv, a.out, a.cmd)
+    elif a.cmd_name == "stats":
         stats(a.csv, a.out, a.cmd)
     else:
         traffic(a.fetch_csv, a.write_csv, a.out, a.calib_mib, a.workload, a.tokens, a.cmd)
