@@ -71,8 +71,9 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}): "
-              "the layer's tokens shard with no exchange, and multi-GPU runs are not part "
-              "of this build", file=sys.stderr)
+              "the layer's tokens shard across GPUs with no exchange, so the figure to "
+              "measure is one GPU's throughput; no multi-GPU path is implemented",
+              file=sys.stderr)
         return 2
 
     import numpy as np
