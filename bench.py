@@ -316,6 +316,34 @@ def measured_traffic(wl, stage):
     return int(v["fetch_size_bytes"] + v["write_size_bytes"])
 
 
+def host_cpu():
+    """Model name (lscpu, else /proc/cpuinfo) and CPU counts of the host."""
+    import subprocess
+
+    model = None
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except (OSError, subprocess.SubprocessError):
+        pass
+    if model is None:
+        try:
+            for line in open("/proc/cpuinfo"):
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+        except OSError:
+            pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except OSError:
+        usable = os.cpu_count()
+    return {"model": model, "cpus": os.cpu_count(), "usable": usable}
+
+
 def cpu_baseline(wl, Wn, x, min_seconds):
     """The float64 oracle forward over layer instance 0's whole token batch, on
     the host, repeated until ``min_seconds`` of CPU time have passed."""
@@ -343,8 +371,10 @@ def cpu_baseline(wl, Wn, x, min_seconds):
             break
     tokens = reps * xs.shape[0]
     log(f"[bench] oracle: {reps} x {xs.shape[0]} tokens in {dt:.2f} s with {threads} BLAS threads")
+    host = host_cpu()
     return {"value": round(tokens / dt, 2), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": host["model"], "host_cpus": host["cpus"],
+            "host_cpus_usable": host["usable"],
             "sample": f"{reps} float64 oracle forward(s) of layer instance 0's {xs.shape[0]} "
                       f"tokens ({wl.name}), {dt:.1f} s of host time"}
 

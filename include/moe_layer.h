@@ -120,7 +120,8 @@ typedef struct moe_layer moe_layer_t;
  * Errors: MOE_ERR_INVALID_ARG (NULL cfg/weights/out, missing weight),
  * MOE_ERR_INVALID_CONFIG (top_k outside 1..E, E > MOE_MAX_EXPERTS, top_k >
  * MOE_MAX_TOP_K, H/I/S/L not multiples of 64 (of 16 for f32 layers),
- * unsupported dtype pair, max_tokens < 1), MOE_ERR_OOM, MOE_ERR_HIP.
+ * H > 8192, unsupported dtype pair, max_tokens < 1, max_tokens * top_k >
+ * 2^30 routes), MOE_ERR_OOM, MOE_ERR_HIP.
  * On error *out is set to NULL. */
 int moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_weights_t* weights,
                      void* stream, moe_layer_t** out);
@@ -166,8 +167,11 @@ int moe_topk_sigmoid(const float* logits, int32_t n, int32_t E, int32_t k, float
 int moe_route_sort(const int32_t* ids, int32_t n, int32_t k, int32_t E, int32_t* counts,
                    int32_t* offsets, int32_t* perm, int32_t* inv, void* stream);
 
-/* Two-level NVFP4 quantizer for weights (page "metrale_model_arch/
- * nemotron_moe.rs": the NVFP4 quantize kernel and ExpertPtrTable layout).
+/* Two-level NVFP4 quantizer for weights, into the storage format of page
+ * "metrale_model_arch/nemotron_moe.rs" (`ExpertPtrTable`: packed table, block
+ * scale table, scale2). The pages print no weight quantizer; this recipe is
+ * the library's reading of the format (the page's own quantize kernel turns
+ * bf16 activations into NVFP4 for the 4-bit x 4-bit GEMMs).
  * w fp32 [G][rows][cols] (cols % 16 == 0) -> packed u8 [G][rows][cols/2],
  * scales u8 [G][rows][cols/16], scale2 fp32 [G], per matrix g:
  *   scale2 = amax|W_g| / 2688, s_b = E4M3_rne(amax_b / (6 * scale2)),

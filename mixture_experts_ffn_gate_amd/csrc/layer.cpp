@@ -178,6 +178,11 @@ int check_config(const moe_layer_config_t& c) {
                 "top_k=%d must be in 1..=%d and at most %d (routing bound)", c.top_k,
                 c.num_experts, MOE_MAX_TOP_K);
   if (c.max_tokens < 1) return fail(MOE_ERR_INVALID_CONFIG, "max_tokens=%d < 1", c.max_tokens);
+  // Routes r = t * top_k + j are 32-bit indices on the device (with headroom
+  // for the tile list and the sort's chunk arithmetic).
+  if ((long long)c.max_tokens * c.top_k > (1LL << 30))
+    return fail(MOE_ERR_INVALID_CONFIG, "max_tokens * top_k = %lld exceeds 2^30 routes",
+                (long long)c.max_tokens * c.top_k);
   const bool f32 = c.act_dtype == MOE_DT_F32;
   if (f32 && c.expert_dtype != MOE_DT_F32)
     return fail(MOE_ERR_INVALID_CONFIG, "fp32 activations need fp32 experts");

@@ -1,7 +1,9 @@
-// NVFP4 weight quantizer on the device (page "metrale_model_arch/nemotron_moe.rs":
-// NVFP4 weights are a packed 4-bit table, a per-block scale table and one
-// per-tensor scale2 per expert; the same page names a bf16 -> NVFP4 quantize
-// kernel). Two-level scheme, every step in fp32:
+// NVFP4 weight quantizer on the device. The storage format follows page
+// "metrale_model_arch/nemotron_moe.rs" (`ExpertPtrTable`: per expert a packed
+// 4-bit table, a per-block scale table and one per-tensor scale2). The pages
+// print no weight quantizer (the quantize kernel they name converts bf16
+// activations for the 4-bit x 4-bit path), so the recipe below is this
+// library's own reading of the format: two levels, every step in fp32:
 //   scale2 = amax|W| / 2688             (2688 = 6 * 448)
 //   s_b    = E4M3_rne(amax_b / (6 * scale2))      per 16 consecutive K
 //   q      = E2M1_rne(w / (e4m3(s_b) * scale2))   saturating at 6

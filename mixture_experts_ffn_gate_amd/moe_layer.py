@@ -158,13 +158,39 @@ class MoeLayer:
         self.num_experts = num_experts
         self.top_k = top_k
 
+    def _check_rows(self, hidden: torch.Tensor, residual: torch.Tensor, num_tokens):
+        """Host-side shape, dtype and device checks of a forward's arguments:
+        the library trusts these pointers, so a mismatch would otherwise be
+        an out-of-bounds device access."""
+        for name, t in (("hidden", hidden), ("residual", residual)):
+            if not isinstance(t, torch.Tensor):
+                raise TypeError(f"{name} must be a torch tensor")
+            if t.dtype != self.act_dtype:
+                raise TypeError(f"{name} is {t.dtype}, the layer's activations are "
+                                f"{self.act_dtype}")
+            if t.dim() != 2 or t.shape[1] != self.hidden_size:
+                raise ValueError(f"{name} must be [N, {self.hidden_size}], got "
+                                 f"{tuple(t.shape)}")
+        if residual.shape != hidden.shape:
+            raise ValueError(f"residual {tuple(residual.shape)} and hidden "
+                             f"{tuple(hidden.shape)} differ")
+        n = hidden.shape[0] if num_tokens is None else int(num_tokens)
+        if n < 0 or n > hidden.shape[0]:
+            raise ValueError(f"num_tokens={n} outside 0..{hidden.shape[0]} (rows of hidden)")
+        for name, t in (("hidden", hidden), ("residual", residual)):
+            if t.device.type != "cuda":
+                raise ValueError(f"{name} must be on a GPU, got {t.device}")
+        return n
+
     def forward(self, hidden: torch.Tensor, residual: torch.Tensor, num_tokens=None,
                 stream=None):
-        n = hidden.shape[0] if num_tokens is None else num_tokens
+        n = self._check_rows(hidden, residual, num_tokens)
         _check(_lib.moe_layer_forward(self._h, _ptr(hidden), _ptr(residual), n, _stream(stream)))
         return hidden
 
     def debug_read(self, which: str, out: torch.Tensor, stream=None):
+        if out.device.type != "cuda":
+            raise ValueError(f"debug_read copies into GPU memory, got {out.device}")
         _check(_lib.moe_layer_debug_read(self._h, DBG[which], _ptr(out),
                                          out.numel() * out.element_size(), _stream(stream)))
         return out
@@ -194,7 +220,19 @@ class MoeLayer:
             pass
 
 
+def _check_tensor(name, t, dtype, dims):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != dims:
+        raise ValueError(f"{name} must have {dims} dimensions, got {tuple(t.shape)}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU, got {t.device}")
+
+
 def topk_sigmoid(logits: torch.Tensor, k: int, scale: float = 1.0, stream=None):
+    _check_tensor("logits", logits, torch.float32, 2)
     n, E = logits.shape
     ids = torch.empty(n, k, dtype=torch.int32, device=logits.device)
     w = torch.empty(n, k, dtype=torch.float32, device=logits.device)
@@ -204,6 +242,7 @@ def topk_sigmoid(logits: torch.Tensor, k: int, scale: float = 1.0, stream=None):
 
 
 def route_sort(ids: torch.Tensor, num_experts: int, stream=None):
+    _check_tensor("ids", ids, torch.int32, 2)
     n, k = ids.shape
     dev = ids.device
     counts = torch.empty(num_experts, dtype=torch.int32, device=dev)
@@ -218,6 +257,7 @@ def route_sort(ids: torch.Tensor, num_experts: int, stream=None):
 def nvfp4_quantize(w: torch.Tensor, stream=None):
     """fp32 [G, rows, cols] -> (packed u8 [G, rows, cols/2], scales u8 [G, rows, cols/16],
     scale2 fp32 [G])."""
+    _check_tensor("w", w, torch.float32, 3)
     G, rows, cols = w.shape
     dev = w.device
     packed = torch.empty(G, rows, cols // 2, dtype=torch.uint8, device=dev)

@@ -54,6 +54,8 @@ def _cfg(mod, **kw):
     (dict(moe_inter=96), -2), (dict(max_tokens=0), -2),
     (dict(act_dtype=0, expert_dtype=1), -2), (dict(act_dtype=7), -2),
     (dict(shared_inter=-64), -2), (dict(hidden_size=16384), -2),
+    # routes are indexed by 32-bit ints: max_tokens * top_k is bounded
+    (dict(max_tokens=600_000_000, top_k=2), -2),
 ])
 def test_create_rejects_bad_config_on_host(mod, kw, code):
     lib = mod.lib()
@@ -109,3 +111,49 @@ def test_profile_kernel_labels():
     assert short_name("_Z11gemv_kernelILi1EDF16bLi0EEv8GemvArgs") == "gemv[store,bf16]"
     assert short_name("_Z11gemv_kernelILi1EDF16bLi1EEv8GemvArgs") == "gemv[store,nvfp4]"
     assert short_name("void route_small_kernel<2>(bool _Accum const*)") == "route_small"
+
+
+def _bare_layer(mod, act_dtype, hidden_size):
+    # A MoeLayer object without a device handle: only its host-side checks run.
+    import torch
+    L = object.__new__(mod.MoeLayer)
+    L._h = None
+    L.act_dtype = act_dtype
+    L.hidden_size = hidden_size
+    return L
+
+
+def test_forward_argument_checks_on_host(mod):
+    import torch
+    L = _bare_layer(mod, torch.bfloat16, 64)
+    h = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        L.forward(h.float(), h)                      # wrong dtype
+    with pytest.raises(TypeError):
+        L.forward(h, h.float())
+    with pytest.raises(ValueError):
+        L.forward(torch.zeros(4, 32, dtype=torch.bfloat16), h)   # wrong width
+    with pytest.raises(ValueError):
+        L.forward(h, torch.zeros(3, 64, dtype=torch.bfloat16))   # residual shape
+    with pytest.raises(ValueError):
+        L.forward(h, h.clone(), num_tokens=5)        # more tokens than rows
+    with pytest.raises(ValueError):
+        L.forward(h, h.clone(), num_tokens=-1)
+    with pytest.raises(ValueError):
+        L.forward(h, h.clone())                      # host memory, not a GPU
+    with pytest.raises(ValueError):
+        L.debug_read("ids", torch.zeros(8, dtype=torch.int32))
+
+
+def test_stage_argument_checks_on_host(mod):
+    import torch
+    with pytest.raises(TypeError):
+        mod.topk_sigmoid(torch.zeros(4, 8, dtype=torch.bfloat16), 2)
+    with pytest.raises(ValueError):
+        mod.topk_sigmoid(torch.zeros(4, 8), 2)        # host memory
+    with pytest.raises(TypeError):
+        mod.route_sort(torch.zeros(4, 2, dtype=torch.int64), 8)
+    with pytest.raises(ValueError):
+        mod.route_sort(torch.zeros(8, dtype=torch.int32), 8)
+    with pytest.raises(TypeError):
+        mod.nvfp4_quantize(torch.zeros(1, 4, 16, dtype=torch.float64))

@@ -63,9 +63,9 @@ def test_topk_stage(ml, n, E, k, ties):
     ids, w = ml.topk_sigmoid(logits.cuda(), k, scale=1.0)
     ids, w = ids.cpu().numpy(), w.cpu().numpy()
     scores = mo.sigmoid_scores(logits.numpy())
-    ref_ids, _ = mo.topk_select(scores, k)
+    ref_ids, tmargin = mo.topk_select(scores, k)
     margin = mo.rank_margin(scores, k)
-    pu.check_ids(ids, ref_ids, margin, max_loose_frac=1.0 if ties else 0.05)
+    pu.check_ids(ids, ref_ids, margin, tmargin, max_loose_frac=1.0 if ties else 0.05)
     same = np.all(ids == ref_ids, axis=1)
     ref_w = mo.routing_weights(scores, ref_ids, 1.0)
     np.testing.assert_allclose(w[same], ref_w[same], rtol=2e-6, atol=1e-7)
@@ -137,12 +137,18 @@ SMALL = {
 }
 
 
+def _cmp(wl, Wn, r, case, rows=None, tol=None):
+    e = pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"], rows=rows, tol=tol,
+                         case=case)
+    print(f"errors {case}: out {e[0]:.3e} delta {e[1]:.3e}", flush=True)
+    return e
+
+
 def test_tiny_f32_full(ml):
     wl = wlm.WORKLOADS["tiny_direct_f32"]
     r = run_layer(ml, wl, wl.N)
     Wn = pu.oracle_weights(r["W"])
-    e = pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"])
-    print("errors", e)
+    _cmp(wl, Wn, r, "tiny_direct_f32 N=64")
 
 
 @pytest.mark.parametrize("name", list(SMALL))
@@ -150,7 +156,7 @@ def test_small_bf16(ml, name):
     wl = SMALL[name]
     r = run_layer(ml, wl, wl.N, seed=5)
     Wn = pu.oracle_weights(r["W"])
-    print("errors", pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"]))
+    _cmp(wl, Wn, r, f"{name} N={wl.N}")
 
 
 @pytest.mark.parametrize("n", [1, 7])
@@ -159,7 +165,7 @@ def test_odd_experts_decode_sizes(ml, n):
     wl = SMALL["odd_experts"]
     r = run_layer(ml, wl, n, seed=12, max_tokens=32)
     Wn = pu.oracle_weights(r["W"])
-    pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"])
+    _cmp(wl, Wn, r, f"odd_experts N={n}")
 
 
 @pytest.mark.parametrize("n", [1, 2, 3, 16, 17, 64])
@@ -167,7 +173,24 @@ def test_small_bf16_token_counts(ml, n):
     wl = SMALL["direct_ragged"]
     r = run_layer(ml, wl, n, seed=11, max_tokens=128)
     Wn = pu.oracle_weights(r["W"])
-    pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"])
+    _cmp(wl, Wn, r, f"direct_ragged N={n}")
+
+
+@pytest.mark.parametrize("n", [1, 5, 16])
+def test_latent_decode_arm(ml, n):
+    # LatentMoE at decode sizes: fc1 GEMV, routed GEMVs in latent space, the
+    # latent reduce into o, and the fc2 GEMV with residual + shared added.
+    wl = SMALL["latent_ragged"]
+    r = run_layer(ml, wl, n, seed=13, max_tokens=32)
+    Wn = pu.oracle_weights(r["W"])
+    _cmp(wl, Wn, r, f"latent_ragged N={n}")
+
+
+def test_latent_decode_arm_nvfp4(ml):
+    wl = NVFP4_SMALL["nvfp4_latent"]
+    r = run_layer(ml, wl, 3, seed=14, max_tokens=16)
+    Wn = pu.oracle_weights(r["W"], nvfp4=True)
+    _cmp(wl, Wn, r, "nvfp4_latent N=3")
 
 
 def test_skewed_routing_many_row_blocks(ml):
@@ -180,7 +203,7 @@ def test_skewed_routing_many_row_blocks(ml):
     r = run_layer(ml, wl, wl.N, W=W, hidden=hidden)
     assert np.bincount(r["ids"].ravel(), minlength=wl.E).max() > 300
     Wn = pu.oracle_weights(W)
-    pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"])
+    _cmp(wl, Wn, r, "skewed N=600")
 
 
 @pytest.mark.parametrize("name", ["direct_ragged", "multiblock_sort", "multiblock_512"])
@@ -203,14 +226,20 @@ def test_sort_stage_bit_exact_inside_forward(ml, name):
         np.testing.assert_array_equal(bufs[nm].cpu().numpy(), ref, err_msg=nm)
 
 
-@pytest.mark.parametrize("name", ["direct_ragged", "latent_ragged"])
-def test_gate_logits_and_normed_inside_forward(ml, name):
-    # The gate is fed the fp32 normed vector (split into bf16 hi + lo parts):
-    # logits agree with the float64 oracle far below the top-k margin bar.
-    wl = SMALL[name]
-    r = run_layer(ml, wl, wl.N, seed=9)
-    logits = torch.empty(wl.N, wl.E, dtype=torch.float32, device="cuda")
-    normed = torch.empty(wl.N, wl.H, dtype=torch.bfloat16, device="cuda")
+WIDE_H = {
+    # 16 rows of H = 5120 or 8192 exceed the LDS staging of the batched
+    # norm+gate kernel: these take norm_gate_mfma_kernel (and, at N <= 16, the
+    # decode routing kernel with more than one load round per wave).
+    "hidden5120": wlm.Workload("hidden5120", H=5120, E=16, k=2, I=128, S=128, L=0, N=40),
+    "hidden8192": wlm.Workload("hidden8192", H=8192, E=24, k=3, I=128, S=64, L=0, N=20),
+    "hidden5120_latent": wlm.Workload("hidden5120_latent", H=5120, E=16, k=2, I=128, S=128,
+                                      L=256, N=70),
+}
+
+
+def _check_logits_normed(r, wl, n):
+    logits = torch.empty(n, wl.E, dtype=torch.float32, device="cuda")
+    normed = torch.empty(n, wl.H, dtype=torch.bfloat16, device="cuda")
     r["layer"].debug_read("logits", logits)
     r["layer"].debug_read("normed", normed)
     torch.cuda.synchronize()
@@ -220,7 +249,26 @@ def test_gate_logits_and_normed_inside_forward(ml, name):
     assert np.max(np.abs(logits.cpu().numpy() - ref)) < 2e-4
     # normed is the bf16 rounding of the fp32 value: within one bf16 ulp.
     nb = f32np(normed)
-    assert np.all(np.abs(nb - n64) <= 2.0 ** -8 * np.abs(n64) + 1e-30)
+    assert np.all(np.abs(nb - n64) <= 2.0 ** -8 * np.abs(n64) * (1 + 1e-5) + 1e-30)
+    return Wn
+
+
+@pytest.mark.parametrize("name", ["direct_ragged", "latent_ragged"])
+def test_gate_logits_and_normed_inside_forward(ml, name):
+    # The gate is fed the fp32 normed vector (split into bf16 hi + lo parts):
+    # logits agree with the float64 oracle far below the top-k margin bar.
+    wl = SMALL[name]
+    r = run_layer(ml, wl, wl.N, seed=9)
+    _check_logits_normed(r, wl, wl.N)
+
+
+@pytest.mark.parametrize("name,n", [("hidden5120", 40), ("hidden5120", 5), ("hidden8192", 20),
+                                    ("hidden8192", 16), ("hidden5120_latent", 70)])
+def test_wide_hidden(ml, name, n):
+    wl = WIDE_H[name]
+    r = run_layer(ml, wl, n, seed=15, max_tokens=max(n, 16))
+    Wn = _check_logits_normed(r, wl, n)
+    _cmp(wl, Wn, r, f"{name} N={n}")
 
 
 def test_residual_input_ignored_and_deterministic(ml):
@@ -254,44 +302,25 @@ def test_errors_and_zero_tokens(ml):
     assert torch.equal(h2, h[:4])
 
 
-def test_graph_capture_replays_match_eager(ml):
+def test_create_out_of_memory(ml):
+    # A workspace far beyond HBM: create must fail with MOE_ERR_OOM, free what
+    # it allocated, and leave the device usable.
+    wl = wlm.Workload("oom", H=8192, E=8, k=2, I=64, S=64, L=0, N=1)
+    W = wlm.make_weights(wl, 0, "cuda")
+    with pytest.raises(ml.MoeError) as ei:
+        ml.layer_from_workload(wl, W, max_tokens=50_000_000)
+    assert ei.value.code == ml.MOE_ERR_OOM
+    small = wl.with_(N=4)
+    r = run_layer(ml, small, 4, W=W)
+    _cmp(small, pu.oracle_weights(W), r, "after OOM N=4")
+
+
+def _capture_and_replay(ml, wl, n, seed):
     # A forward enqueues no host synchronization, allocation or readback, so
-    # it can be captured; replays (with eager work between them) must match.
-    wl = SMALL["latent_ragged"]
-    W = wlm.make_weights(wl, 6, "cuda")
-    h0, _ = wlm.make_hidden(wl, wl.N, 6, "cuda")
-    layer = ml.layer_from_workload(wl, W)
-    eager = h0.clone()
-    res = torch.empty_like(eager)
-    layer.forward(eager, res)
-    torch.cuda.synchronize()
-    hbuf = h0.clone()
-    rbuf = torch.empty_like(hbuf)
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(s):
-        with torch.cuda.graph(graph, stream=s):
-            layer.forward(hbuf, rbuf, stream=s)
-    torch.cuda.synchronize()
-    for rep in range(3):
-        hbuf.copy_(h0)
-        junk = torch.randn(1000, device="cuda").sum()  # eager work between replays
-        graph.replay()
-        torch.cuda.synchronize()
-        assert torch.equal(hbuf, eager), f"replay {rep}"
-        assert torch.equal(rbuf, h0)
-        del junk
-
-
-def test_graph_capture_decode_arm(ml):
-    # The decode-sized arm (one routing kernel whose last block re-arms a
-    # device counter, GEMV launches) captured whole: replays must match the
-    # eager run.
-    wl = SMALL["direct_ragged"]
-    n = 5
-    W = wlm.make_weights(wl, 9, "cuda")
-    h0, _ = wlm.make_hidden(wl, n, 9, "cuda")
+    # it can be captured; replays (with eager work between them) must match
+    # the eager run bit for bit, and the oracle within the bar.
+    W = wlm.make_weights(wl, seed, "cuda")
+    h0, _ = wlm.make_hidden(wl, n, seed, "cuda")
     layer = ml.layer_from_workload(wl, W, max_tokens=n)
     eager = h0.clone()
     res = torch.empty_like(eager)
@@ -306,14 +335,34 @@ def test_graph_capture_decode_arm(ml):
         with torch.cuda.graph(graph, stream=s):
             layer.forward(hbuf, rbuf, stream=s)
     torch.cuda.synchronize()
+    Wn = pu.oracle_weights(W)
+    x = f32np(h0)
     for rep in range(3):
         hbuf.copy_(h0)
-        junk = torch.randn(1000, device="cuda").sum()
+        rbuf.fill_(7.0)
+        junk = torch.randn(1000, device="cuda").sum()  # eager work between replays
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(hbuf, eager), f"replay {rep}"
         assert torch.equal(rbuf, h0)
+        ids = torch.empty(n, wl.k, dtype=torch.int32, device="cuda")
+        layer.debug_read("ids", ids)
+        torch.cuda.synchronize()
+        r = dict(x=x, out=f32np(hbuf), res=f32np(rbuf), ids=ids.cpu().numpy())
+        _cmp(wl, Wn, r, f"{wl.name} N={n} graph replay {rep}")
         del junk
+
+
+def test_graph_capture_replays_match_eager(ml):
+    wl = SMALL["latent_ragged"]
+    _capture_and_replay(ml, wl, wl.N, 6)
+
+
+@pytest.mark.parametrize("name,n", [("direct_ragged", 5), ("latent_ragged", 3)])
+def test_graph_capture_decode_arm(ml, name, n):
+    # The decode-sized arm (one routing kernel whose last block re-arms a
+    # device counter, GEMV launches) captured whole.
+    _capture_and_replay(ml, SMALL[name], n, 9)
 
 
 # ------------------------------------------------ full sizes (bench shapes) --
@@ -330,11 +379,13 @@ def test_full_size_sampled(ml, name):
     wl = wlm.WORKLOADS[name]
     r = run_layer(ml, wl, wl.N, seed=0)
     Wn = pu.oracle_weights(r["W"], lazy_experts=True)
-    # Every token's ids (gate on all rows is cheap), then sampled outputs.
-    ref_ids, margin, _ = pu.oracle_routing(r["x"], Wn, wl)
-    pu.check_ids(r["ids"], ref_ids, margin)
-    rows = _sample_rows(wl.N, 40, 1)
-    print("errors", pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"], rows=rows))
+    # Every token's ids (gate on all rows is cheap), then the outputs of rows
+    # whose routes touch every expert, plus random rows.
+    ref_ids, rmargin, _, tmargin = pu.oracle_routing(r["x"], Wn, wl)
+    pu.check_ids(r["ids"], ref_ids, rmargin, tmargin)
+    rows = pu.rows_covering_experts(r["ids"], wl.E, extra=160, seed=1)
+    assert len(np.unique(r["ids"][rows])) == len(np.unique(r["ids"]))
+    _cmp(wl, Wn, r, f"{name} N={wl.N} ({len(rows)} rows)", rows=rows)
 
 
 def test_wide_tiles_sampled(ml):
@@ -344,10 +395,10 @@ def test_wide_tiles_sampled(ml):
     wl = wlm.Workload("wide_tiles", H=256, E=8, k=2, I=2048, S=4096, L=0, N=4096)
     r = run_layer(ml, wl, wl.N, seed=5)
     Wn = pu.oracle_weights(r["W"])
-    ref_ids, margin, _ = pu.oracle_routing(r["x"], Wn, wl)
-    pu.check_ids(r["ids"], ref_ids, margin)
+    ref_ids, rmargin, _, tmargin = pu.oracle_routing(r["x"], Wn, wl)
+    pu.check_ids(r["ids"], ref_ids, rmargin, tmargin)
     rows = _sample_rows(wl.N, 48, 2)
-    print("errors", pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"], rows=rows))
+    _cmp(wl, Wn, r, "wide_tiles N=4096 (sampled)", rows=rows)
 
 
 def test_six_wave_tiles(ml):
@@ -357,7 +408,7 @@ def test_six_wave_tiles(ml):
     wl = wlm.Workload("six_wave", H=1344, E=64, k=4, I=256, S=128, L=0, N=1024)
     r = run_layer(ml, wl, wl.N, seed=10)
     Wn = pu.oracle_weights(r["W"])
-    print("errors", pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"]))
+    _cmp(wl, Wn, r, "six_wave N=1024")
 
 
 NVFP4_SMALL = {
@@ -375,7 +426,7 @@ def test_small_nvfp4(ml, name):
     wl = NVFP4_SMALL[name]
     r = run_layer(ml, wl, wl.N, seed=7)
     Wn = pu.oracle_weights(r["W"], nvfp4=True)
-    print("errors", pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"]))
+    _cmp(wl, Wn, r, f"{name} N={wl.N}")
 
 
 @pytest.mark.parametrize("n", [1, 5, 16])
@@ -383,7 +434,7 @@ def test_small_nvfp4_decode_sizes(ml, n):
     wl = NVFP4_SMALL["nvfp4_direct"]
     r = run_layer(ml, wl, n, seed=8, max_tokens=64)
     Wn = pu.oracle_weights(r["W"], nvfp4=True)
-    pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"])
+    _cmp(wl, Wn, r, f"nvfp4_direct N={n}")
 
 
 def test_wide_tiles_nvfp4_sampled(ml):
@@ -394,10 +445,10 @@ def test_wide_tiles_nvfp4_sampled(ml):
                       expert_dtype="nvfp4")
     r = run_layer(ml, wl, wl.N, seed=9)
     Wn = pu.oracle_weights(r["W"], nvfp4=True)
-    ref_ids, margin, _ = pu.oracle_routing(r["x"], Wn, wl)
-    pu.check_ids(r["ids"], ref_ids, margin)
+    ref_ids, rmargin, _, tmargin = pu.oracle_routing(r["x"], Wn, wl)
+    pu.check_ids(r["ids"], ref_ids, rmargin, tmargin)
     rows = _sample_rows(wl.N, 48, 3)
-    print("errors", pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"], rows=rows))
+    _cmp(wl, Wn, r, "wide_tiles_nvfp4 N=2048 (sampled)", rows=rows)
 
 
 @pytest.mark.slow
@@ -405,10 +456,15 @@ def test_full_size_nvfp4_sampled(ml):
     wl = wlm.WORKLOADS["nvfp4_direct"]
     r = run_layer(ml, wl, wl.N, seed=0)
     Wn = pu.oracle_weights(r["W"], nvfp4=True, lazy_experts=True)
-    ref_ids, margin, _ = pu.oracle_routing(r["x"], Wn, wl)
-    pu.check_ids(r["ids"], ref_ids, margin)
-    rows = _sample_rows(wl.N, 4, 2)  # each sampled token quantizes its experts in the oracle
-    print("errors", pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"], rows=rows))
+    ref_ids, rmargin, _, tmargin = pu.oracle_routing(r["x"], Wn, wl)
+    pu.check_ids(r["ids"], ref_ids, rmargin, tmargin)
+    rows = pu.rows_covering_experts(r["ids"], wl.E, extra=60, seed=2)
+    touched = np.unique(r["ids"][rows])
+    assert len(touched) == len(np.unique(r["ids"]))
+    # The oracle's own quantization of every touched expert, once, on a pool.
+    Wn["up"].prepare(touched)
+    Wn["down"].prepare(touched)
+    _cmp(wl, Wn, r, f"nvfp4_direct N={wl.N} ({len(rows)} rows)", rows=rows)
 
 
 @pytest.mark.parametrize("n", wlm.DECODE_NS)
@@ -416,4 +472,4 @@ def test_decode_zipf_full(ml, n):
     wl = wlm.WORKLOADS["decode_zipf_bf16"]
     r = run_layer(ml, wl, n, seed=0)
     Wn = pu.oracle_weights(r["W"], lazy_experts=True)
-    print("errors", pu.compare_layer(wl, Wn, r["x"], r["out"], r["res"], r["ids"]))
+    _cmp(wl, Wn, r, f"decode_zipf_bf16 N={n}")
