@@ -167,6 +167,24 @@ int moe_topk_sigmoid(const float* logits, int32_t n, int32_t E, int32_t k, float
 int moe_route_sort(const int32_t* ids, int32_t n, int32_t k, int32_t E, int32_t* counts,
                    int32_t* offsets, int32_t* perm, int32_t* inv, void* stream);
 
+/* Allocation-free form of moe_route_sort, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops and harnesses
+ * that forbid allocation). Same arguments and bit-identical outputs as
+ * moe_route_sort; runs the multi-block form of the sort (the one the layer's
+ * forward uses at large route counts: a per-block expert histogram, then a
+ * stable ballot-ranked scatter per block), whose per-block counts live in a
+ * static device array of MOE_STATIC_SCRATCH_BYTES (1 MiB) that each GPU the
+ * library runs on keeps until the process ends. Nothing is allocated and
+ * nothing in that array needs clearing (every call writes the counts it
+ * reads). Limit: ceil(n*k / 2048) * E <= 262144 (for example n*k up to 4M
+ * routes at E = 128, 1M at E = 512); larger calls return
+ * MOE_ERR_INVALID_ARG before anything is enqueued. Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (other
+ * streams, other threads) race and must be serialized by the caller. */
+#define MOE_STATIC_SCRATCH_BYTES (1 << 20)
+int moe_route_sort_static(const int32_t* ids, int32_t n, int32_t k, int32_t E, int32_t* counts,
+                          int32_t* offsets, int32_t* perm, int32_t* inv, void* stream);
+
 /* Two-level NVFP4 quantizer for weights, into the storage format of page
  * "metrale_model_arch/nemotron_moe.rs" (`ExpertPtrTable`: packed table, block
  * scale table, scale2). The pages print no weight quantizer; this recipe is

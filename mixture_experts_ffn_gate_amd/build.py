@@ -20,7 +20,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_layer.so")
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["routing.hip", "gemm.hip", "reduce.hip", "nvfp4.hip", "layer.cpp"]
+SOURCES = ["routing.hip", "gemm.hip", "reduce.hip", "nvfp4.hip", "scratch.hip", "layer.cpp"]
 
 # -amdgpu-mfma-vgpr-form: MFMA accumulators in ordinary VGPRs. With the
 # default heuristic the compiler kept some in AGPRs and rotated them through

@@ -57,6 +57,13 @@ hipError_t launch_route_sort(const int* ids, int R, int E, int* counts, int* off
                              hipStream_t s);
 int route_sort_blocks(int R);
 
+// Static device scratch (csrc/scratch.hip) of the allocation-free entry
+// points: MOE_STATIC_SCRATCH_INTS ints per device, its device address
+// resolved once per device. Used for the per-block expert counts of the
+// multi-block route sort (route_sort_blocks(R) * E ints).
+#define MOE_STATIC_SCRATCH_INTS (MOE_STATIC_SCRATCH_BYTES / 4)
+hipError_t static_scratch(int** out);
+
 // Decode-sized routing in one launch (bf16, n <= 16): norm + residual + gate,
 // then (last block) top-k and the stable sort. `done` is a zeroed device
 // counter that the kernel leaves at zero.

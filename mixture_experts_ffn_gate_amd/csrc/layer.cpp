@@ -725,6 +725,31 @@ int moe_route_sort(const int32_t* ids, int32_t n, int32_t k, int32_t E, int32_t*
   return MOE_OK;
 }
 
+int moe_route_sort_static(const int32_t* ids, int32_t n, int32_t k, int32_t E, int32_t* counts,
+                          int32_t* offsets, int32_t* perm, int32_t* inv, void* stream) {
+  // Size checks first: nothing below runs for a call the static scratch
+  // cannot hold.
+  if (n < 0 || k < 1) return fail(MOE_ERR_INVALID_ARG, "bad moe_route_sort_static arguments");
+  if (E < 1 || E > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_INVALID_CONFIG, "E=%d outside 1..%d", E, MOE_MAX_EXPERTS);
+  const long long R = (long long)n * k;
+  if (R > (1LL << 30))
+    return fail(MOE_ERR_INVALID_ARG, "n*k = %lld routes exceeds 2^30", R);
+  const long long need = (long long)route_sort_blocks((int)R) * E;
+  if (need > MOE_STATIC_SCRATCH_INTS)
+    return fail(MOE_ERR_INVALID_ARG,
+                "n*k = %lld routes with E=%d need %lld scratch ints, over the static "
+                "scratch of %d (ceil(n*k/2048)*E must be <= %d)",
+                R, E, need, MOE_STATIC_SCRATCH_INTS, MOE_STATIC_SCRATCH_INTS);
+  if (!counts || !offsets || (n > 0 && (!ids || !perm || !inv)))
+    return fail(MOE_ERR_INVALID_ARG, "bad moe_route_sort_static arguments");
+  int* bcnt = nullptr;
+  HIP_TRY(static_scratch(&bcnt));
+  HIP_TRY(launch_route_sort(ids, (int)R, E, counts, offsets, perm, inv, 0, nullptr, nullptr, bcnt,
+                            (hipStream_t)stream));
+  return MOE_OK;
+}
+
 int moe_nvfp4_quantize(const float* w, int32_t G, int32_t rows, int32_t cols, uint8_t* packed,
                        uint8_t* scales, float* scale2, void* stream) {
   if (G < 0 || rows < 0 || cols < 0 || cols % 16 != 0)

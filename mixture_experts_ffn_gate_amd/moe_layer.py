@@ -30,7 +30,7 @@ DBG = dict(normed=0, logits=1, ids=2, weights=3, counts=4, offsets=5, perm=6, in
 # Every function the header declares (checked by the CPU test suite).
 EXPORTS = ("moe_layer_create", "moe_layer_forward", "moe_layer_destroy", "moe_last_error",
            "moe_topk_sigmoid", "moe_route_sort", "moe_nvfp4_quantize", "moe_layer_debug_read",
-           "moe_layer_timing_begin", "moe_layer_timing_end")
+           "moe_layer_timing_begin", "moe_layer_timing_end", "moe_route_sort_static")
 STAGES = ("norm_gate", "shared_up", "shared_down", "fc1", "topk", "sort", "grouped_up",
           "grouped_down", "reduce", "fc2")
 
@@ -77,6 +77,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_topk_sigmoid": (i32, [vp, i32, i32, i32, f32, vp, vp, vp]),
         "moe_route_sort": (i32, [vp, i32, i32, i32, vp, vp, vp, vp, vp]),
+        "moe_route_sort_static": (i32, [vp, i32, i32, i32, vp, vp, vp, vp, vp]),
         "moe_nvfp4_quantize": (i32, [vp, i32, i32, i32, vp, vp, vp, vp]),
         "moe_layer_debug_read": (i32, [vp, i32, vp, i64, vp]),
         "moe_layer_timing_begin": (i32, [vp, ctypes.c_uint32, i32]),
@@ -251,6 +252,21 @@ def route_sort(ids: torch.Tensor, num_experts: int, stream=None):
     inv = torch.empty(n * k, dtype=torch.int32, device=dev)
     _check(_lib.moe_route_sort(_ptr(ids), n, k, num_experts, _ptr(counts), _ptr(offsets),
                                _ptr(perm), _ptr(inv), _stream(stream)))
+    return counts, offsets, perm, inv
+
+
+def route_sort_static(ids: torch.Tensor, num_experts: int, stream=None):
+    """moe_route_sort_static: the same sort with its per-block counts in the
+    library's static device scratch (no allocation inside the library)."""
+    _check_tensor("ids", ids, torch.int32, 2)
+    n, k = ids.shape
+    dev = ids.device
+    counts = torch.empty(num_experts, dtype=torch.int32, device=dev)
+    offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(n * k, dtype=torch.int32, device=dev)
+    inv = torch.empty(n * k, dtype=torch.int32, device=dev)
+    _check(_lib.moe_route_sort_static(_ptr(ids), n, k, num_experts, _ptr(counts), _ptr(offsets),
+                                      _ptr(perm), _ptr(inv), _stream(stream)))
     return counts, offsets, perm, inv
 
 

@@ -157,3 +157,13 @@ def test_stage_argument_checks_on_host(mod):
         mod.route_sort(torch.zeros(8, dtype=torch.int32), 8)
     with pytest.raises(TypeError):
         mod.nvfp4_quantize(torch.zeros(1, 4, 16, dtype=torch.float64))
+
+
+def test_static_sort_rejects_oversize_on_host(mod):
+    # The size check of the allocation-free sort runs before anything else
+    # (NULL pointers here: nothing could be launched even if it did not).
+    lib = mod.lib()
+    assert lib.moe_route_sort_static(None, 65537, 16, 512, None, None, None, None, None) == -1
+    assert "scratch" in lib.moe_last_error().decode()
+    assert lib.moe_route_sort_static(None, 4, 2, 600, None, None, None, None, None) == -2
+    assert lib.moe_route_sort_static(None, 4, 0, 8, None, None, None, None, None) == -1
