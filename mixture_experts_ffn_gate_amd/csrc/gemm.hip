@@ -301,10 +301,12 @@ constexpr int mfma_lds_elems(int stages, int bmt, int cw) {
   return stages * bmt * 64 > bmt * (cw + 8) ? stages * bmt * 64 : bmt * (cw + 8);
 }
 
-// One output tile: BMT rows x (NW waves x WF) features.
+// One output tile: BMT rows x (NW waves x WF) features, of which the first
+// TL 16-row blocks hold live rows (ti.rows <= 16 * TL): the MFMAs and their
+// operand reads skip the padding blocks.
 template <int WF, int BMT, int NW, int EPI, typename TC, int WQ, bool GROUPED, bool NT,
-          bool DEEP>
-__device__ __forceinline__ void mfma_tile(const GemmArgs& a, int slot, int ftile,
+          bool DEEP, int TL>
+__device__ __forceinline__ void mfma_tile(const GemmArgs& a, const TileInfo& ti, int ftile,
                                           bf16* __restrict__ xs) {
   constexpr int S = mfma_stages(BMT, NW, DEEP);
   constexpr int FT = WF / 16;      // 16-feature tiles per wave
@@ -317,14 +319,6 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs& a, int slot, int ftile
   using Frag = typename Src::Frag;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nsteps = a.K / BK;
-  TileInfo ti;
-  if (GROUPED) {
-    if (!decode_tile(a, slot, BMT, ti)) return;  // uniform: no barrier skipped
-  } else {
-    ti.g = 0;
-    ti.row0 = slot * BMT;
-    ti.rows = min(BMT, a.M - ti.row0);
-  }
 
   // Activation loader: chunk c = (tid + threads*i) % CHUNKS -> row c/8,
   // 16-byte chunk c%8 (small tiles: several threads load the same chunk, so
@@ -376,9 +370,9 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs& a, int slot, int ftile
   auto compute = [&](int cur, const Frag& wc) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      bf16x8 xf[TT];
+      bf16x8 xf[TL];
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt) {
+      for (int tt = 0; tt < TL; ++tt) {
         const int row = tt * 16 + brow;
         const int ch = s * 4 + bch;
         xf[tt] = *(const bf16x8*)(&xs[cur * BMT * 64 + row * BK + ((ch ^ (row & 7)) << 3)]);
@@ -387,7 +381,7 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs& a, int slot, int ftile
       for (int ft = 0; ft < FT; ++ft) {
         const bf16x8 wf = src.get(wc, ft, s, lane);
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
+        for (int tt = 0; tt < TL; ++tt)
           acc[ft][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf[tt], acc[ft][tt], 0, 0, 0);
       }
     }
@@ -547,7 +541,26 @@ __global__ void __launch_bounds__(NW * 64, mfma_min_blocks(BMT, NW, DEEP))
       slot = item % inner;
       ftile = o0 + item / inner;
     }
-    mfma_tile<WF, BMT, NW, EPI, TC, WQ, GROUPED, NT, DEEP>(a, slot, ftile, xs);
+    TileInfo ti;
+    if (GROUPED) {
+      if (!decode_tile(a, slot, BMT, ti)) continue;  // uniform: no barrier skipped
+    } else {
+      ti.g = 0;
+      ti.row0 = slot * BMT;
+      ti.rows = min(BMT, a.M - ti.row0);
+    }
+    // Live 16-row blocks, rounded up to a quarter of the tile: a grouped
+    // tile is sized for the larger experts (at 1024 tokens over 128 experts
+    // 57% of the 16-row blocks of the 128-row tiles are padding).
+    constexpr int TT = BMT / 16, Q = TT >= 4 ? TT / 4 : 1;
+    const int ttl = (ti.rows + 15) >> 4;
+    [&]<int... P>(std::integer_sequence<int, P...>) {
+      ((ttl <= (P + 1) * Q || (P + 1) * Q >= TT
+            ? (mfma_tile<WF, BMT, NW, EPI, TC, WQ, GROUPED, NT, DEEP, (P + 1) * Q>(a, ti, ftile, xs),
+               true)
+            : false) ||
+       ...);
+    }(std::make_integer_sequence<int, TT / Q>{});
   }
 }
 
