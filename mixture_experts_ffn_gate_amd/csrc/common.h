@@ -32,30 +32,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Inverse RMS of one bf16 row of H (a multiple of 64), by one wave: every
-// lane sums squares of its 8-element chunks in order (8 chunks in flight, so
-// one round trip up to H = 4096), then the wave reduces. Kernels that must
-// agree bit for bit on a row's scale call this same routine.
-__device__ __forceinline__ float rms_inv_row(const bf16* __restrict__ x, int H, float eps,
-                                             int lane) {
-  float ss = 0.f;
-  for (int i0 = lane * 8; i0 < H; i0 += 512 * 8) {
-    bf16x8 v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      v[u] = i0 + u * 512 < H ? *(const bf16x8*)(x + i0 + u * 512) : bf16x8{};
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float f = (float)v[u][q];
-        ss += f * f;
-      }
-  }
-  ss = wave_sum(ss);
-  return 1.0f / sqrtf(ss / (float)H + eps);
-}
-
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {

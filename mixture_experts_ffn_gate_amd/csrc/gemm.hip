@@ -734,6 +734,8 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemvArgs g) {
   src.init(a, ti.g, nf0, lane);
   const int r = min(lane & 15, ti.rows - 1);
   const bf16* xp = (const bf16*)a.A + (size_t)a_row_of(a, ti.row0 + r) * a.lda + (lane >> 4) * 8;
+  // output row (route order when c_rows is set), loaded before the k-loop
+  const int crow = a.c_rows ? a.c_rows[ti.row0 + r] : ti.row0 + r;
 
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
   // Load groups of GU k-steps dealt round-robin to the 4 waves: at any time
@@ -767,7 +769,7 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemvArgs g) {
   acc += part[2][lane];
   const int n = nf0 + 4 * (lane >> 4);
   const int row = lane & 15;
-  const int p = ti.row0 + row;
+  const int p = crow;  // row == r for every lane that stores
   if (n < a.N && row < ti.rows) {
     if (WQ == 1) acc *= a.b_scale2[ti.g];
     if (EPI == EPI_RELU2) {

@@ -40,6 +40,7 @@ struct GemmArgs {
   const void* res;
   const void* add;  // EPI_ADD_RES second addend, C's dtype (may be null)
   int b_kmajor;     // bf16 weights in the k-major tile order (see launch_retile_bf16)
+  const int* c_rows;  // GEMV arm: output row of row p is c_rows[p] (null: p)
 };
 
 // RMSNorm + residual + gate logits. wgate_t (bf16 layers, may be null) is the
@@ -64,14 +65,16 @@ int route_sort_blocks(int R);
 #define MOE_STATIC_SCRATCH_INTS (MOE_STATIC_SCRATCH_BYTES / 4)
 hipError_t static_scratch(int** out);
 
-// Decode-sized routing in one launch (bf16, n <= 16): norm + residual + gate,
-// then (last block) top-k and the stable sort. `done` is a zeroed device
-// counter that the kernel leaves at zero.
+// Decode-sized routing in one launch (bf16, n <= 16): norm + residual + gate
+// split over expert tiles and hidden slices, then (last block) the logits,
+// top-k and the stable sort. `part` is a workspace of route_small_part_floats()
+// floats; `done` is a zeroed device counter that the kernel leaves at zero.
 hipError_t launch_route_small(const void* hidden, const void* gamma, const void* wgate,
                               void* normed, void* residual, float* logits, int n, int H, int E,
                               float eps, int k, float scale, int* ids, float* w, int* counts,
                               int* offsets, int* perm, int* inv, int bm, int2* tiles,
-                              int* num_tiles, unsigned* done, hipStream_t s);
+                              int* num_tiles, float* part, unsigned* done, hipStream_t s);
+int route_small_part_floats();
 
 // fp32 SIMT GEMM (64x64 tiles, bm must be 64 in grouped mode); C fp32.
 hipError_t launch_gemm_simt_f32(const GemmArgs& a, int epi, int grid_y, hipStream_t s);
@@ -110,6 +113,7 @@ hipError_t launch_retile_nvfp4(const uint8_t* qsrc, const uint8_t* ssrc, uint8_t
 // sh and out are in the activation dtype `dt`; sums run in fp32.
 //   direct: out[t] = residual[t] + sum_j w[t][j] * y[inv[t*k+j]] + sh[t]
 //   latent: out[t] = sum_j w[t][j] * y[inv[t*k+j]]      (res, sh unused)
+// inv == null: y is in route order (row t*k + j).
 hipError_t launch_unpermute_reduce(int dt, bool latent, const void* y, const int* inv,
                                    const float* w, int n, int k, int D, const void* residual,
                                    const void* sh, void* out, hipStream_t s);

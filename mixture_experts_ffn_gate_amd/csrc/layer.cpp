@@ -95,6 +95,7 @@ struct moe_layer {
   int* num_tiles = nullptr;
   int* bcnt = nullptr;    // per-block expert counts of the multi-block sort
   unsigned* sync = nullptr;  // zeroed counter of the decode-sized routing (left at zero)
+  float* rs_part = nullptr;  // partial gate dot products of the decode-sized routing
   hipStream_t side = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   void* g_sh = nullptr;   // shared-expert activation [N][S]
@@ -309,7 +310,7 @@ int forward_small(moe_layer* L, void* hidden, void* residual, int n, hipStream_t
     HIP_TRY(launch_route_small(hidden, L->gamma, L->gate, L->normed, residual, L->logits, n, H,
                                E, c.rms_eps, k, c.routed_scaling_factor, L->ids, L->w,
                                L->counts, L->offsets, L->perm, L->inv, bm, L->tiles,
-                               L->num_tiles, L->sync, s));
+                               L->num_tiles, L->rs_part, L->sync, s));
   }
   const void* zin = L->normed;
   if (Lt > 0) {
@@ -344,6 +345,7 @@ int forward_small(moe_layer* L, void* hidden, void* residual, int n, hipStream_t
     set_weights(L, g[0], L->down, L->down_s, L->down_s2, D, I);
     g[0].C = L->y; g[0].ldc = D; g[0].N = D; g[0].K = I;
     g[0].tiles = L->tiles; g[0].num_tiles = L->num_tiles; g[0].offsets = L->offsets; g[0].bm = bm;
+    g[0].c_rows = L->perm;  // y in route order: the reduce needs no index load
     if (S > 0) {
       g[1].A = L->g_sh; g[1].lda = S; g[1].C = L->sh; g[1].ldc = H;
       g[1].M = n; g[1].N = H; g[1].K = S;
@@ -353,12 +355,12 @@ int forward_small(moe_layer* L, void* hidden, void* residual, int n, hipStream_t
   }
   if (Lt == 0) {
     StageScope sc(L, MOE_STAGE_REDUCE, s);
-    HIP_TRY(launch_unpermute_reduce(c.act_dtype, false, L->y, L->inv, L->w, n, k, D, residual,
+    HIP_TRY(launch_unpermute_reduce(c.act_dtype, false, L->y, nullptr, L->w, n, k, D, residual,
                                     S > 0 ? L->sh : nullptr, hidden, s));
   } else {
     {
       StageScope sc(L, MOE_STAGE_REDUCE, s);
-      HIP_TRY(launch_unpermute_reduce(c.act_dtype, true, L->y, L->inv, L->w, n, k, D, nullptr,
+      HIP_TRY(launch_unpermute_reduce(c.act_dtype, true, L->y, nullptr, L->w, n, k, D, nullptr,
                                       nullptr, L->o, s));
     }
     StageScope sc(L, MOE_STAGE_FC2, s);
@@ -476,6 +478,7 @@ int moe_layer_create(const moe_layer_config_t* cfg, const moe_layer_weights_t* w
   TRY(dalloc(L, (void**)&L->num_tiles, 16));
   TRY(dalloc(L, (void**)&L->bcnt, (size_t)route_sort_blocks((int)R) * E * 4));
   TRY(dalloc(L, (void**)&L->sync, kSyncWords * 4));
+  if (L->mfma) TRY(dalloc(L, (void**)&L->rs_part, (size_t)route_small_part_floats() * 4));
   if (L->mfma) {  // the shared expert's stream (default priority) and its events
     TRYH(hipStreamCreateWithFlags(&L->side, hipStreamNonBlocking));
     TRYH(hipEventCreateWithFlags(&L->ev_fork, hipEventDisableTiming));

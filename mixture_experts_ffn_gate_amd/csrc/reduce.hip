@@ -4,8 +4,9 @@
 // "metrale_model_arch/nemotron_moe.rs", module doc: weighted sum, plus the
 // shared expert, added to hidden).
 //
-// The routed rows y are in expert-sorted order; row inv[t*k + j] holds slot j
-// of token t. Slots are summed in slot order (no atomics), so the result is
+// The routed rows y are in expert-sorted order (row inv[t*k + j] holds slot j
+// of token t), or, from the decode-sized arm, in route order (inv == null:
+// row t*k + j). Slots are summed in slot order (no atomics), so the result is
 // deterministic. Each thread owns 4 consecutive columns; the k slot indices
 // and weights are loaded first so that the k row loads issue together.
 #include "kernels.h"
@@ -40,7 +41,7 @@ __global__ void __launch_bounds__(256) unpermute_reduce_kernel(
 #pragma unroll
   for (int j = 0; j < MOE_MAX_TOPK_REDUCE; ++j)
     if (j < k) {
-      p[j] = inv[t * k + j];
+      p[j] = inv ? inv[t * k + j] : t * k + j;
       wt[j] = w[t * k + j];
     }
 #pragma unroll
@@ -64,13 +65,20 @@ __global__ void __launch_bounds__(1024) unpermute_reduce_bf16_kernel(
   const int t = blockIdx.x;
   const int d = threadIdx.x * 8;
   if (d >= D) return;
+  const size_t o = (size_t)t * D + d;
+  // residual and shared rows do not depend on the slot indices: issued first
+  bf16x8 r = {}, a = {};
+  if (!LATENT) {
+    r = *(const bf16x8*)(residual + o);
+    if (sh) a = *(const bf16x8*)(sh + o);
+  }
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   int p[MOE_MAX_TOPK_REDUCE];
   float wt[MOE_MAX_TOPK_REDUCE];
 #pragma unroll
   for (int j = 0; j < MOE_MAX_TOPK_REDUCE; ++j)
     if (j < k) {
-      p[j] = inv[t * k + j];
+      p[j] = inv ? inv[t * k + j] : t * k + j;
       wt[j] = w[t * k + j];
     }
   bf16x8 v[MOE_MAX_TOPK_REDUCE];
@@ -82,13 +90,10 @@ __global__ void __launch_bounds__(1024) unpermute_reduce_bf16_kernel(
     if (j < k)
 #pragma unroll
       for (int q = 0; q < 8; ++q) acc[q] += wt[j] * (float)v[j][q];
-  const size_t o = (size_t)t * D + d;
   if (!LATENT) {
-    const bf16x8 r = *(const bf16x8*)(residual + o);
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[q] = (float)r[q] + acc[q];
     if (sh) {
-      const bf16x8 a = *(const bf16x8*)(sh + o);
 #pragma unroll
       for (int q = 0; q < 8; ++q) acc[q] += (float)a[q];
     }

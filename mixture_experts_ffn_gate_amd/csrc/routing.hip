@@ -771,92 +771,195 @@ __global__ void __launch_bounds__(512) norm_gate_lds_kernel(const bf16* __restri
 
 // ---------------------------------------------------------------------------
 // Decode-sized routing front end in one launch (N <= 16 tokens, bf16).
-// Block b (16 waves) computes RMSNorm and the gate logits of experts
-// [16b, 16b+16) for all tokens, the k-steps dealt over its 16 waves (same hi+lo
-// fp32 split as the batched kernel) and summed in wave order; block 0 writes
-// normed and residual. The last block to finish (device-scope release fence,
-// then a global counter; acquire fence after) runs the top-k of every token
-// (one wave each) and the one-block stable sort, then re-arms the counter.
-// Device-scope fences write back / invalidate the L2 of the issuing XCD, so
-// each block issues as few as the data flow needs (one wave).
+// The gate projection is split over expert tiles of 16 and slices of the
+// hidden dimension: block (et, hs) of ET x HS (about 64 blocks, 8 waves each)
+// computes the partial dot products W_g[e] . (x_t * gamma) of its 16 experts
+// over its slice of k-steps for all tokens (x * gamma exact in fp32, split
+// into bf16 hi + lo for the MFMA, as in the batched kernel), summed over its
+// waves in wave order, and stores them to `part`. Every block also computes
+// the inverse RMS of every token with the same routine (so every block holds
+// bit-identical values); the blocks of expert tile 0 write their slice of
+// `normed` and `residual`. The last block to finish (release fence, counter,
+// acquire fence) adds the partials over the slices in slice order, scales
+// them by the inverse RMS into the fp32 logits, runs the top-k of every
+// token and a stable sort sized for at most 16 x 16 routes, then re-arms the
+// counter. Device-scope fences write back / invalidate the L2 of the issuing
+// XCD, so only the wave that stored the partials fences.
 // ---------------------------------------------------------------------------
+constexpr int RS_THREADS = 512;   // 8 waves per block
+constexpr int RS_MAX_BLOCKS = 64; // ET * HS bound (sizes the partial buffer)
+constexpr int RS_MAX_R = 16 * MOE_MAX_TOPK_REDUCE;
+
+int route_small_part_floats() { return RS_MAX_BLOCKS * 16 * 16; }  // hs_n * ET <= RS_MAX_BLOCKS
+
+// Stable sort of R <= RS_MAX_R routes (ids in LDS) by expert, one block of
+// RS_THREADS >= E threads: LDS histogram, exclusive scans of counts and row
+// tiles over the experts, then each route's rank among the lower routes of
+// its expert (positions ascend with the route id).
+__device__ void sort_small(const int* __restrict__ sids, int R, int E, int* __restrict__ counts,
+                           int* __restrict__ offsets, int* __restrict__ perm, int* __restrict__ inv,
+                           int bm, int2* __restrict__ tiles, int* __restrict__ num_tiles,
+                           int* __restrict__ cnt, int* __restrict__ base, int (*wsum)[8]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid < E) cnt[tid] = 0;
+  __syncthreads();
+  for (int r = tid; r < R; r += RS_THREADS) atomicAdd(&cnt[sids[r]], 1);
+  __syncthreads();
+  const int c = tid < E ? cnt[tid] : 0;
+  const int tc = tid < E ? (c + bm - 1) / bm : 0;
+  const int ic = wave_incl_scan(c, lane), itc = wave_incl_scan(tc, lane);
+  if (lane == 63) {
+    wsum[0][wave] = ic;
+    wsum[1][wave] = itc;
+  }
+  __syncthreads();
+  int pc = 0, ptc = 0;
+  for (int w = 0; w < wave; ++w) {
+    pc += wsum[0][w];
+    ptc += wsum[1][w];
+  }
+  if (tid < E) {
+    const int excl = pc + ic - c, texcl = ptc + itc - tc;
+    base[tid] = excl;
+    counts[tid] = c;
+    offsets[tid] = excl;
+    if (tid == E - 1) {
+      offsets[E] = excl + c;
+      *num_tiles = texcl + tc;
+    }
+    for (int i = 0; i < tc; ++i) tiles[texcl + i] = make_int2(tid, i * bm);
+  }
+  __syncthreads();
+  for (int r = tid; r < R; r += RS_THREADS) {
+    const int e = sids[r];
+    int rank = 0;
+    for (int q = 0; q < r; ++q) rank += sids[q] == e;
+    const int pos = base[e] + rank;
+    perm[pos] = r;
+    inv[r] = pos;
+  }
+}
+
 template <int EPL>
-__global__ void __launch_bounds__(1024) route_small_kernel(
+__global__ void __launch_bounds__(RS_THREADS) route_small_kernel(
     const bf16* __restrict__ hidden, const bf16* __restrict__ gamma, const bf16* __restrict__ wgate,
     bf16* __restrict__ normed, bf16* __restrict__ residual, float* __restrict__ logits, int n,
     int H, int E, float eps, int k, float scale, int* __restrict__ ids, float* __restrict__ wts,
     int* __restrict__ counts, int* __restrict__ offsets, int* __restrict__ perm,
     int* __restrict__ inv, int bm, int2* __restrict__ tiles, int* __restrict__ num_tiles,
-    unsigned* __restrict__ done) {
+    float* __restrict__ part, int hs_n, unsigned* __restrict__ done) {
   __shared__ float rinv[16];
-  __shared__ floatx4 red[16][64];
-  __shared__ SortLds slds;
-  __shared__ int sids[16 * MOE_MAX_TOPK_REDUCE];
+  __shared__ floatx4 red[8][64];
+  __shared__ float lg[16 * MOE_MAX_E];
+  __shared__ int sids[RS_MAX_R];
+  __shared__ int scnt[MOE_MAX_E], sbase[MOE_MAX_E];
+  __shared__ int wsum[2][8];
   __shared__ int is_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int e0 = blockIdx.x * 16;
+  const int ET = gridDim.x / hs_n;
+  const int et = blockIdx.x % ET, hs = blockIdx.x / ET;
+  const int E16 = ET * 16;
+  const int nsteps = H / 32;
+  const int j0 = hs * nsteps / hs_n, j1 = (hs + 1) * nsteps / hs_n;  // this block's k-steps
+  const int e0 = et * 16;
+  float* pdot = part;  // [hs][16 tokens][E16]
 
-  // 1. inverse RMS: wave t takes token t
-  {
-    const float r = rms_inv_row(hidden + (size_t)min(wave, n - 1) * H, H, eps, lane);
-    if (lane == 0) rinv[wave] = r;
-  }
-  __syncthreads();
-
-  // 2. gate logits of this block's 16 experts; wave w takes k-steps w, w+16, ...
+  // Gate operands: lane holds token tok and k-elements 8*kg..+7 of a 32-wide
+  // k-step; wave w takes k-steps j0 + w, j0 + w + 8, ... of the slice, in
+  // batches of U whose loads issue together. The first batch is issued
+  // before the RMS rows below, so the two load rounds overlap.
   const int tok = lane & 15, kg = lane >> 4;
   const bool tvalid = tok < n;
-  const float rv = rinv[tok];
-  const bool writer = blockIdx.x == 0;
-  const bf16* wrow = wgate + (size_t)min(e0 + tok, E - 1) * H + kg * 8;
+  const bf16* wrow = wgate + (size_t)min(e0 + tok, E - 1) * H + kg * 8;  // rows past E: never stored
   const size_t row = (size_t)tok * H + kg * 8;
-  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-  constexpr int U = 6;  // 84 k-steps of H = 2688 in one round (<= 128 VGPRs per lane)
-  for (int kb = wave * 32; kb < H; kb += 512 * U) {
-    bf16x8 wf[U], xv[U], gv[U];
+  constexpr int U = 4;  // k-steps per load batch
+  bf16x8 wf[U], xv[U], gv[U];
+  auto load_batch = [&](int jb) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int k0 = min(kb + u * 512, H - 32);  // past the end: a valid step, not used
+      const int k0 = min(jb + u * 8, j1 - 1) * 32;  // past the slice: a valid step, not used
       wf[u] = *(const bf16x8*)(wrow + k0);
       xv[u] = tvalid ? *(const bf16x8*)(hidden + row + k0) : bf16x8{};
       gv[u] = *(const bf16x8*)(gamma + k0 + kg * 8);
     }
+  };
+  const int jfirst = j0 + wave;
+  if (jfirst < j1) load_batch(jfirst);
+
+  // 1. inverse RMS of tokens wave and wave + 8 (the same code in every block,
+  //    so every block holds bit-identical values): both rows' loads in one
+  //    round per 2048 elements, each lane summing its chunks in order.
+  if (wave < n) {
+    const bf16* x0 = hidden + (size_t)wave * H;
+    const bf16* x1 = hidden + (size_t)min(wave + 8, n - 1) * H;
+    float s0 = 0.f, s1 = 0.f;
+    for (int i0 = lane * 8; i0 < H; i0 += 512 * 4) {
+      bf16x8 v0[4], v1[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * 512;
+        v0[u] = i < H ? *(const bf16x8*)(x0 + i) : bf16x8{};
+        v1[u] = i < H ? *(const bf16x8*)(x1 + i) : bf16x8{};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float f0 = (float)v0[u][q], f1 = (float)v1[u][q];
+          s0 += f0 * f0;
+          s1 += f1 * f1;
+        }
+    }
+    s0 = wave_sum(s0);
+    s1 = wave_sum(s1);
+    if (lane == 0) {
+      rinv[wave] = 1.0f / sqrtf(s0 / (float)H + eps);
+      if (wave + 8 < n) rinv[wave + 8] = 1.0f / sqrtf(s1 / (float)H + eps);
+    }
+  }
+
+  // 2. partial gate dot products W_g . (x * gamma) over the wave's k-steps
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int jb = jfirst; jb < j1; jb += 8 * U) {
+    if (jb != jfirst) load_batch(jb);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int k0 = kb + u * 512;
-      if (k0 >= H) break;
-      bf16x8 hi, lo, nb;
+      if (jb + u * 8 >= j1) break;
+      bf16x8 hi, lo;
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        const float v = (float)xv[u][q] * rv * (float)gv[u][q];
+        const float v = (float)xv[u][q] * (float)gv[u][q];  // exact: 8-bit x 8-bit mantissas
         hi[q] = (bf16)v;
         lo[q] = (bf16)(v - (float)hi[q]);
-        nb[q] = hi[q];
-      }
-      if (writer && tvalid) {
-        *(bf16x8*)(residual + row + k0) = xv[u];
-        *(bf16x8*)(normed + row + k0) = nb;
       }
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u], hi, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u], lo, acc, 0, 0, 0);
     }
   }
   red[wave][lane] = acc;
-  __syncthreads();
+  __syncthreads();  // also orders rinv
+
+  // residual and normed for this block's slice (expert tile 0 only)
+  if (et == 0) {
+    for (int c = j0 * 4 + (tid & 63); c < j1 * 4; c += 64) {  // 8-element chunks of the slice
+      for (int t = tid >> 6; t < n; t += 8) {
+        const size_t o = (size_t)t * H + c * 8;
+        const bf16x8 xv = *(const bf16x8*)(hidden + o);
+        const bf16x8 gv = *(const bf16x8*)(gamma + c * 8);
+        bf16x8 nb;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) nb[q] = (bf16)((float)xv[q] * rinv[t] * (float)gv[q]);
+        *(bf16x8*)(residual + o) = xv;
+        *(bf16x8*)(normed + o) = nb;
+      }
+    }
+  }
   if (wave == 0) {
     floatx4 v = red[0][lane];
 #pragma unroll
-    for (int w = 1; w < 16; ++w) v += red[w][lane];
-    const int e = e0 + 4 * kg;
-    if (tvalid)
-      for (int q = 0; q < 4; ++q)
-        if (e + q < E) logits[(size_t)tok * E + e + q] = v[q];
-  }
-
-  // 3. the last block finishes routing. Only wave 0 stored logits, so only it
-  // fences (release before the count; acquire after it, in the last block,
-  // ahead of the barrier that orders the other waves' reads).
-  if (wave == 0) {
+    for (int w = 1; w < 8; ++w) v += red[w][lane];
+    *(floatx4*)(pdot + ((size_t)hs * 16 + tok) * E16 + e0 + 4 * kg) = v;
+    // 3. the last block finishes routing (only this wave stored partials)
     __threadfence();
     int last = 0;
     if (lane == 0) last = atomicAdd(done, 1u) == gridDim.x - 1;
@@ -866,14 +969,39 @@ __global__ void __launch_bounds__(1024) route_small_kernel(
   }
   __syncthreads();
   if (!is_last) return;
-  // The ids stay in LDS for the sort (no global round trip), and are copied
-  // out on the side.
-  if (wave < n)
-    topk_token<EPL>(logits + (size_t)wave * E, E, k, scale, sids + wave * k,
-                    wts + (size_t)wave * k, lane);
+
+  // logits = rinv * (sum of the partials in slice order), fp32; a thread
+  // takes 4 consecutive experts of one token, its slices' loads in flight
+  // together (8 at a time)
+  for (int g = tid; g < n * (E16 / 4); g += RS_THREADS) {
+    const int t = g / (E16 / 4), e = (g - t * (E16 / 4)) * 4;
+    const floatx4* src = (const floatx4*)(pdot + (size_t)t * E16 + e);
+    const size_t hstride = (size_t)16 * E16 / 4;
+    floatx4 sum = {0.f, 0.f, 0.f, 0.f};
+    for (int h0 = 0; h0 < hs_n; h0 += 8) {
+      floatx4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = h0 + u < hs_n ? src[(h0 + u) * hstride] : floatx4{};
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (h0 + u < hs_n) sum += v[u];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (e + q < E) {
+        const float l = rinv[t] * sum[q];
+        lg[t * MOE_MAX_E + e + q] = l;
+        logits[(size_t)t * E + e + q] = l;
+      }
+  }
   __syncthreads();
-  if (tid < n * k) ids[tid] = sids[tid];
-  sort_block(sids, n * k, E, counts, offsets, perm, inv, bm, tiles, num_tiles, slds);
+  // top-k: wave w takes tokens w and w + 8
+  for (int t = wave; t < n; t += 8)
+    topk_token<EPL>(lg + t * MOE_MAX_E, E, k, scale, sids + t * k, wts + (size_t)t * k, lane);
+  __syncthreads();
+  const int R = n * k;
+  for (int r = tid; r < R; r += RS_THREADS) ids[r] = sids[r];
+  sort_small(sids, R, E, counts, offsets, perm, inv, bm, tiles, num_tiles, scnt, sbase, wsum);
   if (tid == 0) *done = 0u;
 }
 
@@ -1009,16 +1137,18 @@ hipError_t launch_route_small(const void* hidden, const void* gamma, const void*
                               void* normed, void* residual, float* logits, int n, int H, int E,
                               float eps, int k, float scale, int* ids, float* w, int* counts,
                               int* offsets, int* perm, int* inv, int bm, int2* tiles,
-                              int* num_tiles, unsigned* done, hipStream_t s) {
-  if (n > 16) return hipErrorInvalidValue;
-  dim3 grid((E + 15) / 16);
+                              int* num_tiles, float* part, unsigned* done, hipStream_t s) {
+  if (n < 1 || n > 16 || E > MOE_MAX_E || n * k > RS_MAX_R || bm < 1) return hipErrorInvalidValue;
+  const int ET = (E + 15) / 16, nsteps = H / 32;
+  const int hs_n = std::max(1, std::min(nsteps, RS_MAX_BLOCKS / ET));
+  dim3 grid(ET * hs_n);
   switch ((E + 63) / 64) {
 #define RS_CASE(X)                                                                            \
   case X:                                                                                     \
-    hipLaunchKernelGGL((route_small_kernel<X>), grid, dim3(1024), 0, s, (const bf16*)hidden,    \
+    hipLaunchKernelGGL((route_small_kernel<X>), grid, dim3(RS_THREADS), 0, s, (const bf16*)hidden, \
                        (const bf16*)gamma, (const bf16*)wgate, (bf16*)normed, (bf16*)residual, \
                        logits, n, H, E, eps, k, scale, ids, w, counts, offsets, perm, inv, bm,  \
-                       tiles, num_tiles, done);                                               \
+                       tiles, num_tiles, part, hs_n, done);                                   \
     break;
     RS_CASE(1) RS_CASE(2) RS_CASE(3) RS_CASE(4) RS_CASE(5) RS_CASE(6) RS_CASE(7) RS_CASE(8)
 #undef RS_CASE
