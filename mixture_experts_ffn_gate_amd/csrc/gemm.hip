@@ -173,12 +173,6 @@ __device__ __forceinline__ T ld_w(const T* p) {
   else return *p;
 }
 
-// E4M3 (bias 7, no infinities) scale byte -> fp32 (exact).
-__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
-}
-
 // Eight E2M1 codes (nibble i = element i) times an fp32 block scale -> bf16.
 // e2m1 * e4m3 has at most 6 significant bits, so every product is exact in bf16.
 // gfx950 converts two E2M1 codes (byte j: low nibble first) to fp32 per
@@ -269,9 +263,13 @@ template <int FT, bool NT> struct WSrc<1, FT, NT> {
     }
   }
   __device__ __forceinline__ bf16x8 get(const Frag& f, int ft, int s, int lane) const {
-    // k-chunk s of lane group g = lane/16 lies in block 2s + g/2 of the step.
-    const uint32_t sb = (f.sc[ft] >> (8 * (2 * s + (lane >> 5)))) & 0xFFu;
-    return dequant8(f.q[ft][s], e4m3_to_f32(sb));
+    // k-chunk s of lane group g = lane/16 lies in block 2s + g/2 of the step:
+    // byte 2s of the scale word shifted by 8 * (g/2), decoded by gfx950's
+    // E4M3 (OCP) -> fp32 conversion (exact for all 256 codes).
+    const uint32_t sh = f.sc[ft] >> ((lane >> 5) * 8);
+    const float sc = s == 0 ? __builtin_amdgcn_cvt_f32_fp8((int)sh, 0)
+                            : __builtin_amdgcn_cvt_f32_fp8((int)sh, 2);
+    return dequant8(f.q[ft][s], sc);
   }
 };
 
@@ -368,6 +366,37 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs& a, const TileInfo& ti,
 
   const int brow = lane & 15, bch = lane >> 4;
   auto compute = [&](int cur, const Frag& wc) {
+    if constexpr (TL > 8) {
+      // More than 8 live 16-row blocks: the weight fragments of a half-step
+      // are decoded once, and the activation fragments are read in two
+      // batches (registers).
+      constexpr int CH = (TL + 1) / 2;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        bf16x8 wf[FT];
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft) wf[ft] = src.get(wc, ft, s, lane);
+#pragma unroll
+        for (int c0 = 0; c0 < TL; c0 += CH) {
+          bf16x8 xf[CH];
+#pragma unroll
+          for (int i = 0; i < CH; ++i) {
+            const int row = (c0 + i) * 16 + brow;
+            const int ch = s * 4 + bch;
+            if (c0 + i < TL)
+              xf[i] = *(const bf16x8*)(&xs[cur * BMT * 64 + row * BK + ((ch ^ (row & 7)) << 3)]);
+          }
+#pragma unroll
+          for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+            for (int i = 0; i < CH; ++i)
+              if (c0 + i < TL)
+                acc[ft][c0 + i] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[ft], xf[i], acc[ft][c0 + i], 0, 0, 0);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       bf16x8 xf[TL];
@@ -670,6 +699,10 @@ static hipError_t launch_mfma_wq(const GemmArgs& a, MfmaCfg cfg, int epi, int sl
   if (cfg.wf == W && cfg.bmt == M) return launch_mfma_shape<W, M, 4, WQ, G, NT>(a, epi, slots, s);
   SHAPE(16, 16) SHAPE(32, 32) SHAPE(32, 64)
 #undef SHAPE
+  // 192-row tiles (8 waves, 192 x 256 outputs): grouped NVFP4 launches whose
+  // experts hold up to 192 rows each take one tile per expert.
+  if constexpr (G && WQ == 1)
+    if (cfg.wf == 32 && cfg.bmt == 192) return launch_mfma_shape<32, 192, 8, WQ, G, NT>(a, epi, slots, s);
   return hipErrorInvalidValue;
 }
 
