@@ -27,7 +27,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # The kernel and launch sources, and the build script (its compiler flags
 # change the generated kernels too).
 KERNEL_SOURCES = ("csrc/gemm.hip", "csrc/routing.hip", "csrc/reduce.hip", "csrc/layer.cpp",
-                  "csrc/common.h", "csrc/kernels.h", "build.py")
+                  "csrc/common.h", "csrc/kernels.h", "csrc/wsrc.h", "build.py")
 
 
 def source_hash() -> str:
