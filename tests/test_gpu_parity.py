@@ -159,6 +159,24 @@ def test_small_bf16(ml, name):
     _cmp(wl, Wn, r, f"{name} N={wl.N}")
 
 
+def test_decode_routing_max_routes(ml):
+    # The decode routing kernel at its largest shape: 16 tokens x top-16 = 256
+    # routes over 512 experts (32 expert tiles x 2 hidden slices), every id and
+    # the whole sort stage checked.
+    wl = wlm.Workload("decode_max", H=512, E=512, k=16, I=64, S=64, L=0, N=16)
+    r = run_layer(ml, wl, 16, seed=16)
+    R = 16 * 16
+    bufs = {nm: torch.empty(sz, dtype=torch.int32, device="cuda")
+            for nm, sz in (("counts", wl.E), ("offsets", wl.E + 1), ("perm", R), ("inv", R))}
+    for nm, t in bufs.items():
+        r["layer"].debug_read(nm, t)
+    torch.cuda.synchronize()
+    rc, ro, rp, ri = mo.sort_routes(r["ids"], wl.E)
+    for nm, ref in zip(("counts", "offsets", "perm", "inv"), (rc, ro, rp, ri)):
+        np.testing.assert_array_equal(bufs[nm].cpu().numpy(), ref, err_msg=nm)
+    _cmp(wl, pu.oracle_weights(r["W"]), r, "decode_max N=16")
+
+
 @pytest.mark.parametrize("n", [1, 7])
 def test_odd_experts_decode_sizes(ml, n):
     # decode-size routing kernel with a partial last expert tile
@@ -418,6 +436,10 @@ NVFP4_SMALL = {
                                  expert_dtype="nvfp4"),
     "nvfp4_many_rows": wlm.Workload("nvfp4_many_rows", H=256, E=4, k=2, I=128, S=0, L=0, N=600,
                                     expert_dtype="nvfp4"),
+    # 129-168 rows per expert: 192-row tiles (12 row blocks, operand reads in
+    # two batches, 2-stage ring), one per expert or a second partial one
+    "nvfp4_192rows": wlm.Workload("nvfp4_192rows", H=512, E=8, k=3, I=512, S=128, L=0, N=400,
+                                  expert_dtype="nvfp4"),
 }
 
 
