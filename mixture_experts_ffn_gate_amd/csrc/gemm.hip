@@ -588,9 +588,9 @@ static hipError_t launch_mfma_wq(const GemmArgs& a, MfmaCfg cfg, int epi, int sl
   if (cfg.wf == W && cfg.bmt == M) return launch_mfma_shape<W, M, 4, WQ, G, NT>(a, epi, slots, s);
   SHAPE(16, 16) SHAPE(32, 32) SHAPE(32, 64)
 #undef SHAPE
-  // 192-row tiles (8 waves, 192 x 256 outputs): grouped NVFP4 launches whose
+  // 192-row tiles (8 waves, 192 x 256 outputs): grouped launches whose
   // experts hold up to 192 rows each take one tile per expert.
-  if constexpr (G && WQ == 1)
+  if constexpr (G)
     if (cfg.wf == 32 && cfg.bmt == 192) return launch_mfma_shape<32, 192, 8, WQ, G, NT>(a, epi, slots, s);
   return hipErrorInvalidValue;
 }

@@ -249,15 +249,18 @@ int upload_nvfp4(moe_layer* L, void** q, void** sc, float** s2, const moe_nvfp4_
 // GEMM (the padding rows cost only MFMA time, which the weight stream leaves
 // idle). With fewer experts (one GPU's expert shard: 16) the 128-row grid is
 // too small to fill the chip and 64-row tiles stay 3% faster.
-MfmaCfg grouped_cfg(int rows_per_group, int experts, bool nvfp4) {
-  // NVFP4 weights are decoded in registers once per row tile: from 129 to
-  // 168 rows per expert one 192-row tile per expert decodes each weight once
-  // where a 128-row tile and a second, partial one decoded (and fetched) it
-  // twice (3072 tokens over 128 experts, top-6: grouped up 339 -> 247 us).
-  // Closer to 192 rows half the experts need a second 192-row tile, and the
-  // 128-row tiles (3-stage ring; the 192-row tiles fit 2 stages) were faster
-  // (4096 tokens: 350 vs 384 us).
-  if (nvfp4 && rows_per_group > 128 && rows_per_group <= 168) return {32, 192};
+MfmaCfg grouped_cfg(int rows_per_group, int experts) {
+  // From 97 to 168 rows per expert, one 192-row tile per expert reads (and,
+  // for NVFP4, decodes) each weight slice once, where 128-row tiles gave many
+  // experts a second, partial tile that fetched it again. Measured (bf16):
+  // 2560 / 3072 / 3584 tokens over 128 experts, top-6, 0.819 / 0.925 / 0.978
+  // -> 0.733 / 0.798 / 0.919 ms per layer; the latent layer at 2048 tokens,
+  // top-8 (128 rows per expert), 0.625 -> 0.581 ms; NVFP4 at 3072 tokens
+  // grouped up 339 -> 247 us. At 96 rows per expert and below, and at 192
+  // (half the experts then take a second 192-row tile, and the 192-row tile
+  // fits a 2-stage ring where the 128-row one has 3), 128-row tiles are
+  // faster: 2048 tokens 0.629 vs 0.665 ms, 4096 tokens 0.988 vs 1.085 ms.
+  if (rows_per_group > 96 && rows_per_group <= 168) return {32, 192};
   if (rows_per_group <= 16) return {16, 16};
   if (rows_per_group <= 32) return {32, 32};
   if (rows_per_group <= 40 || (rows_per_group <= 80 && experts < 64)) return {32, 64};
@@ -591,7 +594,7 @@ int moe_layer_forward(moe_layer_t* L, void* hidden, void* residual, int32_t n, v
     StageScope sc(L, MOE_STAGE_TOPK, s);
     HIP_TRY(launch_topk(L->logits, n, E, k, c.routed_scaling_factor, L->ids, L->w, s));
   }
-  MfmaCfg gc = grouped_cfg((R + E - 1) / E, E, L->nvfp4);
+  MfmaCfg gc = grouped_cfg((R + E - 1) / E, E);
   const int bm = bf ? gc.bmt : 64;
   {
     StageScope sc(L, MOE_STAGE_SORT, s);

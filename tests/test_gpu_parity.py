@@ -134,6 +134,10 @@ SMALL = {
     "many_rows": wlm.Workload("many_rows", H=256, E=4, k=2, I=128, S=128, L=0, N=700),
     # E not a multiple of 16 (gate padded with zero rows), H not of 128
     "odd_experts": wlm.Workload("odd_experts", H=320, E=20, k=3, I=128, S=64, L=0, N=90),
+    # 97-168 rows per expert: 192-row tiles (12 row blocks, operand reads in
+    # two batches, 2-stage ring), one per expert or a second partial one
+    "rows_192": wlm.Workload("rows_192", H=512, E=8, k=3, I=512, S=128, L=0, N=400),
+    "latent_192": wlm.Workload("latent_192", H=512, E=8, k=4, I=256, S=256, L=192, N=300),
 }
 
 
