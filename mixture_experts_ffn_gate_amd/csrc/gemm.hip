@@ -470,15 +470,17 @@ __global__ void __launch_bounds__(NW * 64, mfma_min_blocks(BMT, NW, DEEP))
     // Live 16-row blocks, rounded up to a quarter of the tile: a grouped
     // tile is sized for the larger experts (at 1024 tokens over 128 experts
     // 57% of the 16-row blocks of the 128-row tiles are padding).
-    constexpr int TT = BMT / 16, Q = TT >= 4 ? TT / 4 : 1;
+    // The last body covers the whole tile when TT is not a multiple of Q.
+    constexpr int TT = BMT / 16, Q = TT >= 4 ? TT / 4 : 1, NQ = (TT + Q - 1) / Q;
     const int ttl = (ti.rows + 15) >> 4;
     [&]<int... P>(std::integer_sequence<int, P...>) {
-      ((ttl <= (P + 1) * Q || (P + 1) * Q >= TT
-            ? (mfma_tile<WF, BMT, NW, EPI, TC, WQ, GROUPED, NT, DEEP, (P + 1) * Q>(a, ti, ftile, xs),
+      ((ttl <= (P + 1) * Q || P + 1 == NQ
+            ? (mfma_tile<WF, BMT, NW, EPI, TC, WQ, GROUPED, NT, DEEP, std::min((P + 1) * Q, TT)>(
+                   a, ti, ftile, xs),
                true)
             : false) ||
        ...);
-    }(std::make_integer_sequence<int, TT / Q>{});
+    }(std::make_integer_sequence<int, NQ>{});
   }
 }
 
