@@ -742,6 +742,125 @@ hipError_t launch_gemv(const GemmArgs* segs, const int* slots, int nseg, int epi
 }
 
 // ---------------------------------------------------------------------------
+// Decode-sized down projection fused with the weighted reduce (direct
+// layers): out[t] = residual[t] + sum over routes (t, j) of w[t*k+j] *
+// (h[route] . W_down[expert]) + shared_down(g_sh[t]) (page "Struct MoeLayer",
+// `forward_prefill`: down GEMM, unpermute, weighted reduce, shared expert
+// added; page "metrale_model_arch/nemotron_moe.rs", module doc: routed
+// weighted sum plus the shared expert, added to hidden).
+// One workgroup per 16 output features. Its waves take whole items: the
+// routed 16-row tiles of the decode tile list (one expert each) and the
+// shared expert's k-range splits, dealt round-robin. Each wave adds the
+// routing-weighted results of its items into its own [token][feature] LDS
+// partial (a tile holds distinct tokens, so the lanes of a wave never
+// collide); the partials are summed in wave order and added to the residual
+// once, in fp32, so the result is deterministic and the routed outputs never
+// leave the CU.
+// ---------------------------------------------------------------------------
+template <int WQ>
+__global__ void __launch_bounds__(GEMV_REDUCE_WAVES * 64) gemv_down_reduce_kernel(GemvReduceArgs g) {
+  constexpr int NWV = GEMV_REDUCE_WAVES;
+  constexpr int RING = 6;  // k-steps in flight per wave
+  using Src = WSrc<WQ, 1, true>;
+  using Frag = typename Src::Frag;
+  __shared__ floatx4 part[NWV][16][4];  // [wave][token][4-feature group]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n0 = blockIdx.x * 16;
+  const int r = lane & 15, fg = lane >> 4;
+  part[wave][r][fg] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const GemmArgs& ra = g.routed;
+  const int nt = *ra.num_tiles;
+  const int items = nt + g.shared_splits;
+  for (int it = wave; it < items; it += NWV) {
+    const bool routed = it < nt;
+    // the item's operand fields, selected per field (a reference to either
+    // kernel argument would place them in scratch memory)
+    GemmArgs a;
+    a.A = routed ? ra.A : g.shared.A;
+    a.lda = routed ? ra.lda : g.shared.lda;
+    a.B = routed ? ra.B : g.shared.B;
+    a.b_gstride = routed ? ra.b_gstride : g.shared.b_gstride;
+    a.b_scales = routed ? ra.b_scales : g.shared.b_scales;
+    a.bs_gstride = routed ? ra.bs_gstride : g.shared.bs_gstride;
+    a.b_scale2 = routed ? ra.b_scale2 : g.shared.b_scale2;
+    a.N = routed ? ra.N : g.shared.N;
+    a.K = routed ? ra.K : g.shared.K;
+    a.b_kmajor = routed ? ra.b_kmajor : g.shared.b_kmajor;
+    int grp, row0, rows, k0, k1;
+    if (routed) {
+      TileInfo ti;
+      if (!decode_tile(ra, it, 16, ti)) continue;  // uniform per wave
+      grp = ti.g; row0 = ti.row0; rows = ti.rows;
+      k0 = 0; k1 = a.K / 64;
+    } else {
+      const int sp = it - nt, ks = a.K / 64;
+      grp = 0; row0 = 0; rows = g.n;
+      k0 = (int)((long long)ks * sp / g.shared_splits);
+      k1 = (int)((long long)ks * (sp + 1) / g.shared_splits);
+    }
+    Src src;
+    src.init(a, grp, n0, lane);
+    const bf16* xp =
+        (const bf16*)a.A + (size_t)(row0 + min(r, rows - 1)) * a.lda + fg * 8;
+    // Rolling ring of RING k-steps per wave: the loads of step ks + RING are
+    // issued as soon as step ks has been consumed, so a wave (one workgroup
+    // per CU here) keeps RING steps in flight through the whole k-range.
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    Frag wv[RING];
+    bf16x8 x[RING][2];
+    auto load = [&](int slot_ks, Frag& f, bf16x8* xs2) __attribute__((always_inline)) {
+      const int ks = min(slot_ks, k1 - 1);  // past the range: a valid step, not used
+      src.load(f, ks);
+      xs2[0] = *(const bf16x8*)(xp + ks * 64);
+      xs2[1] = *(const bf16x8*)(xp + ks * 64 + 32);
+    };
+#pragma unroll
+    for (int u = 0; u < RING; ++u) load(k0 + u, wv[u], x[u]);
+    for (int kb = k0; kb < k1; kb += RING) {
+#pragma unroll
+      for (int u = 0; u < RING; ++u) {
+        if (kb + u < k1) {
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(src.get(wv[u], 0, s, lane), x[u][s],
+                                                          acc, 0, 0, 0);
+          if (kb + u + RING < k1) load(kb + u + RING, wv[u], x[u]);
+        }
+      }
+    }
+    // lane: features n0 + 4*fg .. +3 of tile row r
+    if (r < rows) {
+      if (WQ == 1) acc *= a.b_scale2[grp];
+      int t = r;
+      if (routed) {
+        const int rid = g.perm[row0 + r];
+        t = rid / g.k;
+        acc *= g.w[rid];
+      }
+      part[wave][t][fg] += acc;
+    }
+  }
+  __syncthreads();
+  if (wave != 0 || r >= g.n) return;
+  floatx4 sum = part[0][r][fg];
+#pragma unroll
+  for (int w = 1; w < NWV; ++w) sum += part[w][r][fg];
+  const size_t o = (size_t)r * g.ldo + n0 + 4 * fg;
+  sum = store4<bf16>::ld(g.residual + o) + sum;
+  store4<bf16>::st(g.out + o, sum);
+}
+
+hipError_t launch_gemv_down_reduce(const GemvReduceArgs& g, int D, bool nvfp4, hipStream_t s) {
+  if (D % 16 != 0 || g.n < 1 || g.n > 16) return hipErrorInvalidValue;
+  const dim3 grid(D / 16), block(GEMV_REDUCE_WAVES * 64);
+  if (nvfp4)
+    hipLaunchKernelGGL(gemv_down_reduce_kernel<1>, grid, block, 0, s, g);
+  else
+    hipLaunchKernelGGL(gemv_down_reduce_kernel<0>, grid, block, 0, s, g);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Re-tile [G][N][K] row-major bf16 into the MFMA A-operand lane order:
 // feature-major [G][N/16][K/32][64][8] or k-major [G][K/64][N/16][2][64][8].
 // One thread per 16-byte destination chunk.

@@ -94,6 +94,25 @@ hipError_t launch_gemm_mfma(const GemmArgs& a, MfmaCfg cfg, int epi, bool tc_bf1
 // Decode-sized GEMV arm (row tiles of <= 16 rows, bf16 activations and
 // output): nseg (1 or 2) segments in one launch, each with `slots` row tiles;
 // grouped segments set `tiles`.
+// Decode-sized down projection fused with the weighted reduce, residual
+// and shared-expert add (direct layers, n <= 16): routed.A = h in decode
+// tile-list order (tiles of <= 16 rows), routed.B the down weights; shared.A
+// = shared up output [n][S], shared.B its down weights (shared_splits = 0:
+// no shared expert). perm maps a tile-list row to its route t*k + j, w the
+// route weights. out may alias neither residual nor the inputs.
+constexpr int GEMV_REDUCE_WAVES = 8;
+struct GemvReduceArgs {
+  GemmArgs routed;
+  GemmArgs shared;
+  int shared_splits;  // k-range splits of the shared expert (0: none)
+  const int* perm;
+  const float* w;
+  int k, n;
+  const bf16* residual;
+  bf16* out;
+  int ldo;
+};
+hipError_t launch_gemv_down_reduce(const GemvReduceArgs& g, int D, bool nvfp4, hipStream_t s);
 hipError_t launch_gemv(const GemmArgs* segs, const int* slots, int nseg, int epi, bool nvfp4,
                        hipStream_t s);
 

@@ -309,6 +309,22 @@ def test_residual_input_ignored_and_deterministic(ml):
     assert torch.equal(outs[0][1], h0) and torch.equal(outs[1][1], h0)
 
 
+@pytest.mark.parametrize("name", ["no_shared", "direct_ragged", "topk_all"])
+def test_one_token_fused_down_reduce(ml, name):
+    # One token runs the down projection, weighted reduce, shared expert and
+    # residual add as one launch (per-wave LDS partials summed in wave order):
+    # without a shared expert, with one, and with more items (8 routes + 1
+    # shared split) than waves. Run twice on the same inputs: bit-identical.
+    wl = SMALL[name]
+    r = run_layer(ml, wl, 1, seed=21, max_tokens=8)
+    _cmp(wl, pu.oracle_weights(r["W"]), r, f"{name} N=1 (fused down + reduce)")
+    h = r["hidden"].clone()
+    h.copy_(torch.from_numpy(r["x"]).to(h.dtype))
+    r["layer"].forward(h, torch.empty_like(h))
+    torch.cuda.synchronize()
+    assert np.array_equal(f32np(h), r["out"])
+
+
 def test_errors_and_zero_tokens(ml):
     wl = SMALL["no_shared"]
     W = wlm.make_weights(wl, 0, "cuda")
