@@ -445,7 +445,19 @@ __global__ void __launch_bounds__(NW * 64, mfma_min_blocks(BMT, NW, DEEP))
   const int o0 = xcd * chunk;
   const int items = max(0, min(chunk, outer - o0)) * inner;
   const int nrows = max(0, min(chunk, outer - o0));
-  for (int item = blockIdx.x >> 3; item < items; item += wg_per_xcd) {
+  // Grouped launches with a.sched take their items dynamically: after its
+  // first item (blockIdx.x >> 3) a workgroup takes the next unclaimed item
+  // of its XCD from a.sched[xcd] (claimed at the start of the current item,
+  // so the atomic's latency hides under it), which evens out items of
+  // different lengths (partial feature tiles, experts of different row
+  // counts). The last workgroup of each XCD to finish re-arms both counters
+  // for the next launch (a.sched[8 + xcd] counts finished workgroups).
+  const bool dyn = GROUPED && a.sched != nullptr;
+  __shared__ int s_next[2];  // alternating: one barrier per item suffices
+  int item = blockIdx.x >> 3;
+  for (int it = 0; item < items; ++it) {
+    unsigned claimed = 0;
+    if (dyn && threadIdx.x == 0) claimed = atomicAdd(&a.sched[xcd], 1u);
     int slot, ftile;
     if (rows_major) {
       // groups of RG row tiles; inside a group the RG row tiles of one feature
@@ -460,27 +472,43 @@ __global__ void __launch_bounds__(NW * 64, mfma_min_blocks(BMT, NW, DEEP))
       ftile = o0 + item / inner;
     }
     TileInfo ti;
+    bool live_tile = true;
     if (GROUPED) {
-      if (!decode_tile(a, slot, BMT, ti)) continue;  // uniform: no barrier skipped
+      live_tile = decode_tile(a, slot, BMT, ti);  // uniform
     } else {
       ti.g = 0;
       ti.row0 = slot * BMT;
       ti.rows = min(BMT, a.M - ti.row0);
     }
-    // Live 16-row blocks, rounded up to a quarter of the tile: a grouped
-    // tile is sized for the larger experts (at 1024 tokens over 128 experts
-    // 57% of the 16-row blocks of the 128-row tiles are padding).
-    // The last body covers the whole tile when TT is not a multiple of Q.
-    constexpr int TT = BMT / 16, Q = TT >= 4 ? TT / 4 : 1, NQ = (TT + Q - 1) / Q;
-    const int ttl = (ti.rows + 15) >> 4;
-    [&]<int... P>(std::integer_sequence<int, P...>) {
-      ((ttl <= (P + 1) * Q || P + 1 == NQ
-            ? (mfma_tile<WF, BMT, NW, EPI, TC, WQ, GROUPED, NT, DEEP, std::min((P + 1) * Q, TT)>(
-                   a, ti, ftile, xs),
-               true)
-            : false) ||
-       ...);
-    }(std::make_integer_sequence<int, NQ>{});
+    if (live_tile) {
+      // Live 16-row blocks, rounded up to a quarter of the tile: a grouped
+      // tile is sized for the larger experts (at 1024 tokens over 128 experts
+      // 57% of the 16-row blocks of the 128-row tiles are padding).
+      // The last body covers the whole tile when TT is not a multiple of Q.
+      constexpr int TT = BMT / 16, Q = TT >= 4 ? TT / 4 : 1, NQ = (TT + Q - 1) / Q;
+      const int ttl = (ti.rows + 15) >> 4;
+      [&]<int... P>(std::integer_sequence<int, P...>) {
+        ((ttl <= (P + 1) * Q || P + 1 == NQ
+              ? (mfma_tile<WF, BMT, NW, EPI, TC, WQ, GROUPED, NT, DEEP,
+                           std::min((P + 1) * Q, TT)>(a, ti, ftile, xs),
+                 true)
+              : false) ||
+         ...);
+      }(std::make_integer_sequence<int, NQ>{});
+    }
+    if (dyn) {
+      if (threadIdx.x == 0) s_next[it & 1] = wg_per_xcd + (int)claimed;
+      __syncthreads();
+      item = s_next[it & 1];
+    } else {
+      item += wg_per_xcd;
+    }
+  }
+  if (dyn && threadIdx.x == 0) {
+    if (atomicAdd(&a.sched[8 + xcd], 1u) == (unsigned)wg_per_xcd - 1) {
+      atomicExch(&a.sched[xcd], 0u);
+      atomicExch(&a.sched[8 + xcd], 0u);
+    }
   }
 }
 

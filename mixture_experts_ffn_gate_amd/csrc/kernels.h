@@ -41,6 +41,11 @@ struct GemmArgs {
   const void* add;  // EPI_ADD_RES second addend, C's dtype (may be null)
   int b_kmajor;     // bf16 weights in the k-major tile order (see launch_retile_bf16)
   const int* c_rows;  // GEMV arm: output row of row p is c_rows[p] (null: p)
+  // Grouped MFMA launches: 16 zeroed counters (per-XCD next item, per-XCD
+  // finished workgroups; left at zero by the launch) for dynamic item
+  // scheduling, or null for the static schedule. Launches sharing one array
+  // must not overlap.
+  unsigned* sched;
 };
 
 // RMSNorm + residual + gate logits. wgate_t (bf16 layers, may be null) is the

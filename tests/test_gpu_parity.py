@@ -396,6 +396,14 @@ def test_graph_capture_replays_match_eager(ml):
     _capture_and_replay(ml, wl, wl.N, 6)
 
 
+def test_graph_capture_dynamic_item_order(ml):
+    # Experts of several row tiles: the grouped launches take their items
+    # from per-XCD counters that each launch re-arms; every replay must
+    # still match the eager run bit for bit.
+    wl = SMALL["many_rows"]
+    _capture_and_replay(ml, wl, wl.N, 9)
+
+
 @pytest.mark.parametrize("name,n", [("direct_ragged", 5), ("latent_ragged", 3)])
 def test_graph_capture_decode_arm(ml, name, n):
     # The decode-sized arm (one routing kernel whose last block re-arms a
