@@ -304,6 +304,8 @@ def measured_traffic(wl, stage):
     wq = "nvfp4" if wl.expert_dtype == "nvfp4" else "bf16"
     prefix = (f"gemv[{role},{wq}]" if wl.N <= GEMV_MAX_N and wl.act_dtype == "bf16"
               else f"gemm[grouped,{role},{wq},")
+    if wl.N == 1 and wl.L == 0 and wl.act_dtype == "bf16" and stage == "grouped_down":
+        prefix = "gemv_down_reduce"  # one token: down projection fused with the reduce
     if rec.get("tokens") != wl.N:
         return None
     cands = [(v.get("dispatches", 0), v) for k, v in rec["kernels"].items()

@@ -76,7 +76,8 @@ def short_name(name: str) -> str:
     if m:
         epi, mid, norm = m.groups()
         return f"gemv[{_EPI.get(epi, epi)},{_wq(mid)}]"
-    for key in ("route_small", "norm_gate", "topk_sigmoid", "route_sort", "route_hist",
+    for key in ("gemv_down_reduce", "route_small", "norm_gate", "topk_sigmoid", "route_sort",
+                "route_hist",
                 "route_scatter", "unpermute_reduce", "retile", "nvfp4_pack", "nvfp4_scale2",
                 "copyBuffer"):
         if key in name:
