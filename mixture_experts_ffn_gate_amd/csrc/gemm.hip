@@ -255,10 +255,11 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs& a, const TileInfo& ti,
 
   const int brow = lane & 15, bch = lane >> 4;
   auto compute = [&](int cur, const Frag& wc) {
-    if constexpr (TL > 8) {
-      // More than 8 live 16-row blocks: the weight fragments of a half-step
-      // are decoded once, and the activation fragments are read in two
-      // batches (registers).
+    if constexpr (TL > 8 || (WQ == 1 && FT >= 3 && TL > 4)) {
+      // More than 8 live 16-row blocks, or NVFP4 waves of three or more
+      // feature tiles: the weight fragments of a half-step are decoded once,
+      // and the activation fragments are read in two batches (registers: the
+      // 48-feature NVFP4 tile spilled 48 B/lane with all eight at once).
       constexpr int CH = (TL + 1) / 2;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -606,6 +607,14 @@ static hipError_t launch_mfma_wq(const GemmArgs& a, MfmaCfg cfg, int epi, int sl
         };
         if (cost(192) < cost(256)) return launch_mfma_shape<32, 128, 6, WQ, G, NT>(a, epi, slots, s);
       }
+    // Grouped NVFP4 launches of two tiles per CU or more take 48 features per
+    // wave (8 waves, 128 x 384 outputs): each activation fragment read from
+    // LDS feeds three MFMAs instead of two, and the weights (4.5 bits each,
+    // decoded in registers) cost few registers. 2688 = 7 x 384; 1856 in 4.8
+    // tiles. Measured 1024 / 2048 / 4096 / 8192 tokens: 0.401 / 0.509 /
+    // 0.878 / 1.567 -> 0.382 / 0.486 / 0.820 / 1.450 ms.
+    if constexpr (G && WQ == 1)
+      if (items8 >= 2LL * cus) return launch_mfma_shape<48, 128, 8, WQ, G, NT>(a, epi, slots, s);
     if (items8 >= 2LL * cus || dense8)
       return launch_mfma_shape<32, 128, 8, WQ, G, NT>(a, epi, slots, s);
     // A dense bf16 launch with at most one tile per CU runs one workgroup per

@@ -1,6 +1,6 @@
-// Weight fragment sources of the MFMA kernels (GEMM, GEMV, and the decode
-// routing kernel's shared-expert tiles): bf16 weights pre-tiled to the MFMA
-// lane order, or NVFP4 weights decoded in registers to exact bf16.
+// Weight fragment sources of the MFMA kernels (GEMM, GEMV, and the fused
+// one-token down projection): bf16 weights pre-tiled to the MFMA lane order,
+// or NVFP4 weights decoded in registers to exact bf16.
 #pragma once
 
 #include "common.h"
@@ -85,26 +85,36 @@ template <int FT, bool NT> struct WSrc<0, FT, NT> {
 
 template <int FT, bool NT> struct WSrc<1, FT, NT> {
   struct Frag { u32x2 q[FT]; uint32_t sc[FT]; };
-  const u32x2* pq[FT];
-  const uint32_t* ps[FT];
-  int live[FT];  // 1 for a live tile, 0 for a dead one (fixed address, zero step)
+  // Wave-uniform group bases and per-tile offsets (scalar registers; callers
+  // pass a wave-uniform nf0), one per-lane offset: each load is a scalar base
+  // + vector offset address (the 48-feature tiles had spilled with a 64-bit
+  // pointer pair per feature tile).
+  const u32x2* qg;
+  const uint32_t* sg;
+  int qoff[FT], soff[FT], qstep[FT], sstep[FT];
+  int lq, ls;
   __device__ __forceinline__ void init(const GemmArgs& a, int g, int nf0, int lane) {
-    const uint8_t* Q = (const uint8_t*)a.B + (size_t)g * a.b_gstride;
-    const uint8_t* S = a.b_scales + (size_t)g * a.bs_gstride;
+    qg = (const u32x2*)((const uint8_t*)a.B + (size_t)g * a.b_gstride);
+    sg = (const uint32_t*)(a.b_scales + (size_t)g * a.bs_gstride);
     const int KS = a.K / 64;
+    nf0 = __builtin_amdgcn_readfirstlane(nf0);
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) {
       const int rt = (nf0 >> 4) + ft;
-      live[ft] = rt * 16 < a.N;
-      pq[ft] = (const u32x2*)Q + (live[ft] ? (size_t)rt * KS * 64 + lane : 0);
-      ps[ft] = (const uint32_t*)S + (live[ft] ? (size_t)rt * KS * 16 + (lane & 15) : 0);
+      const bool live = rt * 16 < a.N;
+      qoff[ft] = live ? rt * KS * 64 : 0;
+      soff[ft] = live ? rt * KS * 16 : 0;
+      qstep[ft] = live ? 64 : 0;
+      sstep[ft] = live ? 16 : 0;
     }
+    lq = lane;
+    ls = lane & 15;
   }
   __device__ __forceinline__ void load(Frag& f, int ks) const {
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) {
-      f.q[ft] = ld_w<NT>(pq[ft] + (size_t)ks * 64 * live[ft]);
-      f.sc[ft] = ps[ft][(size_t)ks * 16 * live[ft]];
+      f.q[ft] = ld_w<NT>(qg + (qoff[ft] + ks * qstep[ft]) + lq);
+      f.sc[ft] = sg[(soff[ft] + ks * sstep[ft]) + ls];
     }
   }
   __device__ __forceinline__ bf16x8 get(const Frag& f, int ft, int s, int lane) const {

@@ -468,6 +468,11 @@ NVFP4_SMALL = {
     # two batches, 2-stage ring), one per expert or a second partial one
     "nvfp4_192rows": wlm.Workload("nvfp4_192rows", H=512, E=8, k=3, I=512, S=128, L=0, N=400,
                                   expert_dtype="nvfp4"),
+    # 512 items of 128 x 256: the up projection takes 48-feature waves (128 x
+    # 384 tiles; 2048 = 5.33 tiles, the last one partly dead), batched operand
+    # reads, two row tiles per expert in dynamic item order
+    "nvfp4_wide48": wlm.Workload("nvfp4_wide48", H=256, E=32, k=4, I=2048, S=256, L=0, N=2048,
+                                 expert_dtype="nvfp4"),
 }
 
 
