@@ -58,7 +58,10 @@ __global__ void __launch_bounds__(256) unpermute_reduce_kernel(
 // bf16: one workgroup per token, 8 columns (16 bytes) per thread; the k slot
 // indices and weights are the same for the whole workgroup. Same summation
 // order as above (slots in order, then residual, then shared).
-template <bool LATENT>
+// KMAX: the slot arrays' size (8 covers top-k <= 8 with half the registers
+// of the general 16: more resident waves, measured 45.2 -> 39.4 us at 4096
+// tokens, 15.9 -> 14.5 us at 1024).
+template <bool LATENT, int KMAX>
 __global__ void __launch_bounds__(1024) unpermute_reduce_bf16_kernel(
     const bf16* __restrict__ y, const int* __restrict__ inv, const float* __restrict__ w, int k,
     int D, const bf16* __restrict__ residual, const bf16* __restrict__ sh, bf16* __restrict__ out) {
@@ -73,20 +76,20 @@ __global__ void __launch_bounds__(1024) unpermute_reduce_bf16_kernel(
     if (sh) a = *(const bf16x8*)(sh + o);
   }
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  int p[MOE_MAX_TOPK_REDUCE];
-  float wt[MOE_MAX_TOPK_REDUCE];
+  int p[KMAX];
+  float wt[KMAX];
 #pragma unroll
-  for (int j = 0; j < MOE_MAX_TOPK_REDUCE; ++j)
+  for (int j = 0; j < KMAX; ++j)
     if (j < k) {
       p[j] = inv ? inv[t * k + j] : t * k + j;
       wt[j] = w[t * k + j];
     }
-  bf16x8 v[MOE_MAX_TOPK_REDUCE];
+  bf16x8 v[KMAX];
 #pragma unroll
-  for (int j = 0; j < MOE_MAX_TOPK_REDUCE; ++j)
+  for (int j = 0; j < KMAX; ++j)
     if (j < k) v[j] = *(const bf16x8*)(y + (size_t)p[j] * D + d);
 #pragma unroll
-  for (int j = 0; j < MOE_MAX_TOPK_REDUCE; ++j)
+  for (int j = 0; j < KMAX; ++j)
     if (j < k)
 #pragma unroll
       for (int q = 0; q < 8; ++q) acc[q] += wt[j] * (float)v[j][q];
@@ -110,14 +113,15 @@ hipError_t launch_unpermute_reduce(int dt, bool latent, const void* y, const int
   if (k > MOE_MAX_TOPK_REDUCE) return hipErrorInvalidValue;
   if (dt == MOE_DT_BF16 && D % 8 == 0 && D / 8 <= 1024) {
     const dim3 block(((D / 8) + 63) / 64 * 64);
-    if (latent)
-      hipLaunchKernelGGL((unpermute_reduce_bf16_kernel<true>), dim3(n), block, 0, s,
-                         (const bf16*)y, inv, w, k, D, (const bf16*)residual, (const bf16*)sh,
-                         (bf16*)out);
-    else
-      hipLaunchKernelGGL((unpermute_reduce_bf16_kernel<false>), dim3(n), block, 0, s,
-                         (const bf16*)y, inv, w, k, D, (const bf16*)residual, (const bf16*)sh,
-                         (bf16*)out);
+#define RED_LAUNCH(L, KM)                                                                       \
+  hipLaunchKernelGGL((unpermute_reduce_bf16_kernel<L, KM>), dim3(n), block, 0, s, (const bf16*)y, \
+                     inv, w, k, D, (const bf16*)residual, (const bf16*)sh, (bf16*)out)
+    if (k <= 8) {
+      if (latent) RED_LAUNCH(true, 8); else RED_LAUNCH(false, 8);
+    } else {
+      if (latent) RED_LAUNCH(true, MOE_MAX_TOPK_REDUCE); else RED_LAUNCH(false, MOE_MAX_TOPK_REDUCE);
+    }
+#undef RED_LAUNCH
     return hipGetLastError();
   }
   dim3 grid(n, (D / 4 + 255) / 256);
