@@ -356,13 +356,14 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs& a, const TileInfo& ti,
       for (int tt = 0; tt < TT; ++tt) {
         floatx4 v = acc[ft][tt];
         if (WQ == 1) v *= s2;
-        if (EPI == EPI_RELU2) {
+        const int c = wave * WF + ft * 16 + 4 * (lane >> 4);
+        if (EPI == EPI_RELU2 && (GROUPED || a.relu_n == 0 || ftile * CW + c < a.relu_n)) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) v[q] = relu2(v[q]);
         }
         bf16x4 o;
         o[0] = (bf16)v[0]; o[1] = (bf16)v[1]; o[2] = (bf16)v[2]; o[3] = (bf16)v[3];
-        const int r = tt * 16 + (lane & 15), c = wave * WF + ft * 16 + 4 * (lane >> 4);
+        const int r = tt * 16 + (lane & 15);
         *(bf16x4*)(&xs[r * SP + c]) = o;
       }
     __syncthreads();

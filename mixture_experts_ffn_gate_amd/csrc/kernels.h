@@ -46,6 +46,9 @@ struct GemmArgs {
   // scheduling, or null for the static schedule. Launches sharing one array
   // must not overlap.
   unsigned* sched;
+  // Dense EPI_RELU2 launches: relu^2 only on output columns < relu_n (0: all
+  // columns; a multiple of 4 otherwise).
+  int relu_n;
 };
 
 // RMSNorm + residual + gate logits. wgate_t (bf16 layers, may be null) is the
