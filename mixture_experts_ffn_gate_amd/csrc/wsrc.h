@@ -55,30 +55,36 @@ template <int WQ, int FT, bool NT> struct WSrc;
 // both tile orders.
 template <int FT, bool NT> struct WSrc<0, FT, NT> {
   struct Frag { bf16x8 v[FT][2]; };
-  const bf16* p[FT];
+  // Wave-uniform group base and per-tile offsets and steps (elements; scalar
+  // registers), one per-lane offset shared by the tiles.
+  const bf16* wg;
+  int off[FT];
   int step[FT];  // elements per 64-wide k-step (0 for a dead tile)
+  int loff;
   __device__ __forceinline__ void init(const GemmArgs& a, int g, int nf0, int lane) {
-    const bf16* W = (const bf16*)a.B + (size_t)g * a.b_gstride;
+    wg = (const bf16*)a.B + (size_t)g * a.b_gstride;
     const int KC = a.K / 32;
+    nf0 = __builtin_amdgcn_readfirstlane(nf0);
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) {
       const int rt = (nf0 >> 4) + ft;
       const bool live = rt * 16 < a.N;
       if (a.b_kmajor) {  // [K/64][N/16][2][64][8]
-        p[ft] = live ? W + ((size_t)rt * 2 * 64 + lane) * 8 : W;
+        off[ft] = live ? rt * 2 * 64 * 8 : 0;
         step[ft] = live ? (a.N / 16) * 1024 : 0;
       } else {  // [N/16][K/32][64][8]
-        p[ft] = live ? W + ((size_t)rt * KC * 64 + lane) * 8 : W;
+        off[ft] = live ? rt * KC * 64 * 8 : 0;
         step[ft] = live ? 1024 : 0;
       }
     }
+    loff = lane * 8;
   }
   __device__ __forceinline__ void load(Frag& f, int ks) const {
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-        f.v[ft][s] = ld_w<NT>((const bf16x8*)(p[ft] + (size_t)ks * step[ft] + s * 512));
+        f.v[ft][s] = ld_w<NT>((const bf16x8*)(wg + (off[ft] + ks * step[ft] + s * 512) + loff));
   }
   __device__ __forceinline__ bf16x8 get(const Frag& f, int ft, int s, int) const { return f.v[ft][s]; }
 };
