@@ -255,11 +255,12 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs& a, const TileInfo& ti,
 
   const int brow = lane & 15, bch = lane >> 4;
   auto compute = [&](int cur, const Frag& wc) {
-    if constexpr (TL > 8 || (WQ == 1 && FT >= 3 && TL > 4)) {
-      // More than 8 live 16-row blocks, or NVFP4 waves of three or more
-      // feature tiles: the weight fragments of a half-step are decoded once,
-      // and the activation fragments are read in two batches (registers: the
-      // 48-feature NVFP4 tile spilled 48 B/lane with all eight at once).
+    if constexpr (TL > 8 || (FT >= 3 && TL > 4)) {
+      // More than 8 live 16-row blocks, or waves of three or more feature
+      // tiles: the weight fragments of a half-step are decoded once, and the
+      // activation fragments are read in two batches (registers: with all
+      // eight at once the 48-feature tiles spilled, NVFP4 48 B/lane, bf16
+      // 170-210 B/lane).
       constexpr int CH = (TL + 1) / 2;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -616,10 +617,11 @@ static hipError_t launch_mfma_wq(const GemmArgs& a, MfmaCfg cfg, int epi, int sl
     // 0.878 / 1.567 -> 0.382 / 0.486 / 0.820 / 1.450 ms.
     if constexpr (G && WQ == 1)
       if (items8 >= 2LL * cus) return launch_mfma_shape<48, 128, 8, WQ, G, NT>(a, epi, slots, s);
-    // Dense NVFP4 launches take the 48-feature waves where their 1.5x longer
-    // items need fewer item-time rounds (NVFP4 shared down at 4096 tokens:
-    // 224 items in one round instead of 352 in two, 102 -> 77 us).
-    if constexpr (!G && WQ == 1) {
+    // Dense launches take the 48-feature waves where their 1.5x longer items
+    // need fewer item-time rounds (224 items in one round instead of 352 in
+    // two: shared down at 4096 tokens, NVFP4 102 -> 77 us, bf16 94 -> 78 us;
+    // bf16 shared up at 16384 tokens 5 rounds instead of 8, 332 -> 312 us).
+    if constexpr (!G) {
       const long long items48 = (long long)slots * ((a.N + 383) / 384);
       const long long r32 = (items8 + cus - 1) / cus, r48 = (items48 + cus - 1) / cus;
       if (items8 >= cus && 3 * r48 < 2 * r32)

@@ -447,6 +447,20 @@ def test_wide_tiles_sampled(ml):
     _cmp(wl, Wn, r, "wide_tiles N=4096 (sampled)", rows=rows)
 
 
+def test_dense_wide48_sampled(ml):
+    # Dense bf16 launches on 48-feature waves (128 x 384 tiles) where that
+    # needs fewer item rounds: 48 row tiles x 1344 features (3.5 tiles of 384,
+    # the last one half dead) for the shared up (relu^2), the shared down
+    # (store) and fc2 (residual + shared epilogue); ragged last row tile.
+    wl = wlm.Workload("dense_wide48", H=1344, E=8, k=2, I=128, S=1344, L=256, N=6100)
+    r = run_layer(ml, wl, wl.N, seed=11)
+    Wn = pu.oracle_weights(r["W"])
+    ref_ids, rmargin, _, tmargin = pu.oracle_routing(r["x"], Wn, wl)
+    pu.check_ids(r["ids"], ref_ids, rmargin, tmargin)
+    rows = np.union1d(_sample_rows(wl.N, 48, 4), np.arange(wl.N - 84, wl.N))
+    _cmp(wl, Wn, r, "dense_wide48 N=6100 (sampled)", rows=rows)
+
+
 def test_six_wave_tiles(ml):
     # Grouped down projection 1344 = 7 x 192 wide with one 128-row tile per
     # expert (64 rows each): 6-wave workgroups, 4 k-steps (the 3-stage ring's
