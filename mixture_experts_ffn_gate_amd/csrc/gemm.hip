@@ -614,9 +614,16 @@ static hipError_t launch_mfma_wq(const GemmArgs& a, MfmaCfg cfg, int epi, int sl
     // LDS feeds three MFMAs instead of two, and the weights (4.5 bits each,
     // decoded in registers) cost few registers. 2688 = 7 x 384; 1856 in 4.8
     // tiles. Measured 1024 / 2048 / 4096 / 8192 tokens: 0.401 / 0.509 /
-    // 0.878 / 1.567 -> 0.382 / 0.486 / 0.820 / 1.450 ms.
-    if constexpr (G && WQ == 1)
-      if (items8 >= 2LL * cus) return launch_mfma_shape<48, 128, 8, WQ, G, NT>(a, epi, slots, s);
+    // 0.878 / 1.567 -> 0.382 / 0.486 / 0.820 / 1.450 ms. So do grouped bf16
+    // launches over experts of several row tiles (the MFMAs, not the weight
+    // stream, bound them) where 384-wide tiles pad N no more than 256-wide
+    // ones (1856 and 2688 yes, 1024 no): direct layer at 4096 / 8192 / 16384
+    // tokens 0.943 / 1.661 / 3.009 -> 0.892 / 1.575 / 2.838 ms; the latent
+    // down projection (1024 wide) had lost 8% on them.
+    if constexpr (G && (WQ == 1 || !NT))
+      if (items8 >= 2LL * cus &&
+          (WQ == 1 || (a.N + 383) / 384 * 384 <= (a.N + 255) / 256 * 256))
+        return launch_mfma_shape<48, 128, 8, WQ, G, NT>(a, epi, slots, s);
     // Dense launches take the 48-feature waves where their 1.5x longer items
     // need fewer item-time rounds (224 items in one round instead of 352 in
     // two: shared down at 4096 tokens, NVFP4 102 -> 77 us, bf16 94 -> 78 us;

@@ -447,6 +447,19 @@ def test_wide_tiles_sampled(ml):
     _cmp(wl, Wn, r, "wide_tiles N=4096 (sampled)", rows=rows)
 
 
+def test_grouped_wide48_sampled(ml):
+    # Grouped bf16 launches over experts of several row tiles (about 1024 rows
+    # each, ragged last tiles, dynamic item order) on 48-feature waves:
+    # 1152 = 3 x 384 for both projections, 640 items each.
+    wl = wlm.Workload("grouped_wide48", H=1152, E=16, k=4, I=1152, S=256, L=0, N=4096)
+    r = run_layer(ml, wl, wl.N, seed=12)
+    Wn = pu.oracle_weights(r["W"])
+    ref_ids, rmargin, _, tmargin = pu.oracle_routing(r["x"], Wn, wl)
+    pu.check_ids(r["ids"], ref_ids, rmargin, tmargin)
+    rows = pu.rows_covering_experts(r["ids"], wl.E, extra=48, seed=3)
+    _cmp(wl, Wn, r, "grouped_wide48 N=4096 (sampled)", rows=rows)
+
+
 def test_dense_wide48_sampled(ml):
     # Dense bf16 launches on 48-feature waves (128 x 384 tiles) where that
     # needs fewer item rounds: 48 row tiles x 1344 features (3.5 tiles of 384,
