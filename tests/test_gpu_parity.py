@@ -404,10 +404,11 @@ def test_graph_capture_dynamic_item_order(ml):
     _capture_and_replay(ml, wl, wl.N, 9)
 
 
-@pytest.mark.parametrize("name,n", [("direct_ragged", 5), ("latent_ragged", 3)])
+@pytest.mark.parametrize("name,n", [("direct_ragged", 5), ("latent_ragged", 3), ("direct_ragged", 1)])
 def test_graph_capture_decode_arm(ml, name, n):
     # The decode-sized arm (one routing kernel whose last block re-arms a
-    # device counter, GEMV launches) captured whole.
+    # device counter, GEMV launches; at one token the fused down projection
+    # and reduce) captured whole.
     _capture_and_replay(ml, SMALL[name], n, 9)
 
 
