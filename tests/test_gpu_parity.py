@@ -435,6 +435,23 @@ def test_full_size_sampled(ml, name):
     _cmp(wl, Wn, r, f"{name} N={wl.N} ({len(rows)} rows)", rows=rows)
 
 
+@pytest.mark.slow
+def test_full_size_direct_4096_sampled(ml):
+    # The direct shapes at 4096 tokens: experts of about 192 rows (two row
+    # tiles, dynamic item order) on 128 x 384 grouped tiles, and the shared
+    # down projection on 128 x 384 dense tiles. Every id, the rows covering
+    # every expert plus random rows.
+    wl = wlm.WORKLOADS["nemotron_direct_bf16"]
+    n = 4096
+    r = run_layer(ml, wl, n, seed=4, max_tokens=n)
+    Wn = pu.oracle_weights(r["W"], lazy_experts=True)
+    ref_ids, rmargin, _, tmargin = pu.oracle_routing(r["x"], Wn, wl)
+    pu.check_ids(r["ids"], ref_ids, rmargin, tmargin)
+    rows = pu.rows_covering_experts(r["ids"], wl.E, extra=64, seed=4)
+    assert len(np.unique(r["ids"][rows])) == len(np.unique(r["ids"]))
+    _cmp(wl, Wn, r, f"nemotron_direct_bf16 N={n} ({len(rows)} rows)", rows=rows)
+
+
 def test_wide_tiles_sampled(ml):
     # 128-row tiles with 8 waves per workgroup (grouped up: 1024 rows per
     # expert; shared up: 32 row tiles x 16 feature tiles) next to 4-wave
