@@ -175,8 +175,10 @@ template <> struct store4<bf16> {
 // register budget of a whole SIMD: 8-10% on the shared expert at 1024
 // tokens); two elsewhere (three cost 2-5% on 64-row tiles, and spill at two
 // 128 x 128 workgroups per CU).
+// The 7-wave tiles (48 features per wave) keep two stages: with three their
+// activation loads (three 16-byte chunks per thread) spill.
 constexpr int mfma_stages(int bmt, int nw, bool deep) {
-  return deep || (bmt == 128 && nw >= 6) ? 3 : 2;
+  return deep || (bmt == 128 && (nw == 6 || nw == 8)) ? 3 : 2;
 }
 // Workgroups per CU the register budget is sized for.
 constexpr int mfma_min_blocks(int bmt, int nw, bool deep) {
@@ -592,22 +594,27 @@ static hipError_t launch_mfma_wq(const GemmArgs& a, MfmaCfg cfg, int epi, int sl
     const bool dense8 = !G && items8 >= (long long)cus &&
                         (a.N % 256 == 0 || 2 * items8 >= 3LL * cus);
     // Weight-streaming grouped bf16 launches (each expert one row tile) take
-    // 6 waves (192 features per workgroup) where that needs less time per XCD
-    // than 8, with one workgroup per CU either way: rounds of items x (features
-    // per item + a fixed 128-feature equivalent per item), a fit to the two
-    // projections at 1024 and 2048 tokens. The 2688-wide down projection goes
-    // from 6 rounds of 256 (last feature tile half dead) to 7 of 192 (238 ->
-    // 224 us); the 1856-wide up projection keeps 4 rounds of 256 (5 of 192
-    // measured 218 -> 225 us). Where the MFMAs bound the launch, the uneven
-    // waves per SIMD cost 10-20%, so NVFP4 weights and multi-tile experts keep
-    // 8 waves.
+    // the feature width that needs the least time per XCD, with one
+    // workgroup per CU for each: rounds of items x (features per item + a
+    // fixed 128-feature equivalent per item), a fit to the two projections at
+    // 1024 and 2048 tokens. 336 features (7 waves of 48) only where they
+    // divide N: the 2688-wide down projection goes from 6 rounds of 256 (last
+    // feature tile half dead) to 7 of 192 (238 -> 224 us) and to 4 of 336
+    // (220 -> 210 us; 2048 tokens 237 -> 215 us); the 1856-wide up
+    // projection keeps 4 rounds of 256 (5 of 192 measured 218 -> 225 us, 5 of
+    // 384 210 -> 221 us). Where the MFMAs bound the launch, the uneven waves
+    // per SIMD cost 10-20%, so NVFP4 weights and multi-tile experts keep 8
+    // waves.
     if constexpr (G && NT && WQ == 0)
       if (cfg.est_tiles > 0 && items8 >= 2LL * cus) {
         const long long t = (cfg.est_tiles + 7) / 8, w = std::max(1, cus / 8);
         auto cost = [&](long long width) {
           return (t * ((a.N + width - 1) / width) + w - 1) / w * (width + 128);
         };
-        if (cost(192) < cost(256)) return launch_mfma_shape<32, 128, 6, WQ, G, NT>(a, epi, slots, s);
+        const long long c192 = cost(192), c256 = cost(256);
+        if (a.N % 336 == 0 && cost(336) < std::min(c192, c256))
+          return launch_mfma_shape<48, 128, 7, WQ, G, NT>(a, epi, slots, s);
+        if (c192 < c256) return launch_mfma_shape<32, 128, 6, WQ, G, NT>(a, epi, slots, s);
       }
     // Grouped NVFP4 launches of two tiles per CU or more take 48 features per
     // wave (8 waves, 128 x 384 outputs): each activation fragment read from

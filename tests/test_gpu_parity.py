@@ -492,6 +492,20 @@ def test_dense_wide48_sampled(ml):
     _cmp(wl, Wn, r, "dense_wide48 N=6100 (sampled)", rows=rows)
 
 
+def test_seven_wave_tiles(ml):
+    # Grouped down projection 1344 = 4 x 336 wide with one 128-row tile per
+    # expert (64 rows each, 128 experts): 7-wave workgroups of 48-feature
+    # waves (128 x 336 tiles), 2-stage ring. Every token's ids; the outputs of
+    # rows covering every expert plus random rows.
+    wl = wlm.Workload("seven_wave", H=1344, E=128, k=4, I=256, S=128, L=0, N=2048)
+    r = run_layer(ml, wl, wl.N, seed=13)
+    Wn = pu.oracle_weights(r["W"])
+    ref_ids, rmargin, _, tmargin = pu.oracle_routing(r["x"], Wn, wl)
+    pu.check_ids(r["ids"], ref_ids, rmargin, tmargin)
+    rows = pu.rows_covering_experts(r["ids"], wl.E, extra=96, seed=5)
+    _cmp(wl, Wn, r, "seven_wave N=2048 (sampled)", rows=rows)
+
+
 def test_six_wave_tiles(ml):
     # Grouped down projection 1344 = 7 x 192 wide with one 128-row tile per
     # expert (64 rows each): 6-wave workgroups, 4 k-steps (the 3-stage ring's
