@@ -507,13 +507,14 @@ def test_seven_wave_tiles(ml):
 
 
 def test_six_wave_tiles(ml):
-    # Grouped down projection 1344 = 7 x 192 wide with one 128-row tile per
-    # expert (64 rows each): 6-wave workgroups, 4 k-steps (the 3-stage ring's
-    # tail only). Every token compared.
-    wl = wlm.Workload("six_wave", H=1344, E=64, k=4, I=256, S=128, L=0, N=1024)
+    # Grouped down projection 1152 = 6 x 192 wide (4.5 tiles of 256; 336 does
+    # not divide it) with one 128-row tile per expert (64 rows each, 128
+    # experts): 6-wave workgroups, 4 k-steps (the 3-stage ring's tail only).
+    # Every token compared.
+    wl = wlm.Workload("six_wave", H=1152, E=128, k=4, I=256, S=128, L=0, N=2048)
     r = run_layer(ml, wl, wl.N, seed=10)
     Wn = pu.oracle_weights(r["W"])
-    _cmp(wl, Wn, r, "six_wave N=1024")
+    _cmp(wl, Wn, r, "six_wave N=2048")
 
 
 NVFP4_SMALL = {
