@@ -108,6 +108,11 @@ def test_profile_kernel_labels():
                       "(GemmArgs, int, int, int, int)") == "gemm[grouped,relu2,nvfp4,128x128]"
     assert short_name("void gemm_mfma_kernel<32, 128, 4, 1, bool _Accum, int, E, false, false, false>"
                       "(GemmArgs, int, int, int, int)") == "gemm[dense,store,nvfp4,128x128]"
+    # 48-feature waves: 8 x 48 = 384 and 7 x 48 = 336 features per workgroup
+    assert short_name("_Z16gemm_mfma_kernelILi48ELi128ELi7ELi1EDF16bLi0ELb1ELb1ELb0EEv8GemmArgsiiii") \
+        == "gemm[grouped,store,bf16,336x128,nt]"
+    assert short_name("_Z16gemm_mfma_kernelILi48ELi128ELi8ELi2EDF16bLi0ELb0ELb0ELb0EEv8GemmArgsiiii") \
+        == "gemm[dense,add_res,bf16,384x128]"
     assert short_name("_Z11gemv_kernelILi1EDF16bLi0EEv8GemvArgs") == "gemv[store,bf16]"
     assert short_name("_Z11gemv_kernelILi1EDF16bLi1EEv8GemvArgs") == "gemv[store,nvfp4]"
     assert short_name("void route_small_kernel<2>(bool _Accum const*)") == "route_small"
